@@ -1,0 +1,244 @@
+"""Benchmark of the Star Attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+context KV write, phase 1 (blockwise-local causal attention with the anchor),
+the phase-2 query step (KV append, split partials, LSE merge) and the
+autoregressive decode loop (n_decode steps of append + partials + merge).
+
+Prints ONE JSON line. ``value`` is the phase-1 context throughput (tokens/s)
+measured inside the timed steps; the decode figure (µs per step and per
+token) is reported beside it. ``roofline`` is for the dominant kernel
+(phase 1, MFMA-bound), ``roofline_phase2`` for the decode partial kernel
+(HBM-bound); both are computed from HIP events recorded on the launch stream
+around every launch of that kernel in the timed steps. ``cpu_baseline`` is
+the fp64 oracle timed on a bounded sample on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "phase-1 ctx tokens/s + phase-2 decode µs/token at 128K, % of roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def phase1_flops(w) -> float:
+    """Algorithmic FLOPs of phase 1: 4*d per visible (query, key) pair, per head."""
+    pairs = 0
+    for i in range(w.n_blocks):
+        bl = min(w.block_len, w.ctx_len - i * w.block_len)
+        pairs += bl * (bl + 1) // 2 + (w.anchor_len * bl if i > 0 else 0)
+    return 4.0 * w.head_dim * pairs * w.batch * w.n_q_heads
+
+
+def decode_bytes(w, kv_len: int, n_split: int) -> float:
+    """Algorithmic HBM bytes of one decode partial launch: K+V rows [0, kv_len),
+    the query rows, and the fp32 partials written."""
+    elt = 2 if w.dtype == "bf16" else 4
+    kv = 2.0 * w.batch * w.n_kv_heads * kv_len * w.head_dim * elt
+    q = w.batch * w.n_q_heads * w.head_dim * elt
+    parts = w.batch * w.n_q_heads * n_split * (w.head_dim + 1) * 4
+    return kv + q + parts
+
+
+def cpu_baseline(w, inputs, budget_s: float = 12.0):
+    """The oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+
+    from long_context_attention_phase1_amd import synthetic as syn
+    from oracle import star_oracle as orc
+
+    rng = np.random.default_rng(0)
+    G = w.group
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    rows = rng.integers(0, w.ctx_len, size=4096)
+    # exact widening of the inputs, outside the timed region
+    wide = (syn.bf16_bits_to_f32 if w.dtype == "bf16" else np.asarray)
+    Ks = [wide(inputs["k_ctx"][0, :, g]) for g in range(w.n_kv_heads)]
+    Vs = [wide(inputs["v_ctx"][0, :, g]) for g in range(w.n_kv_heads)]
+    t0, c0 = time.perf_counter(), time.process_time()
+    done = 0
+    for r in rows:
+        r = int(r)
+        for g in range(w.n_kv_heads):
+            q = wide(inputs["q_ctx"][0, r:r + 1, g * G:(g + 1) * G])
+            orc.phase1_rows_one_head(q, Ks[g], Vs[g], [r], w.block_len, w.anchor_len, sc)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {"value": done / wall, "unit": "ctx tokens/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"phase-1 fp64 oracle on {done} context rows drawn uniformly (seed 0) "
+                      f"from sequence 0, all {w.n_q_heads} query heads, {wall:.1f} s wall"}
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH/WRITE counters, if
+    they were taken on the current kernel source; else None."""
+    try:
+        doc = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = doc.get(kernel)
+    if not ent:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "long_context_attention_phase1_amd", "csrc", "star_kernels.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if ent.get("source_sha256_16") != h:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b_128k_peaked")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threads", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the path is measured on one GPU's share "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_attention_phase1_amd as sa
+    from long_context_attention_phase1_amd import synthetic as syn
+    from tests.gpu_pipeline import Pipeline
+
+    w = syn.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    inputs = syn.make_inputs(w, args.threads)
+    p = Pipeline(w, inputs=inputs, fill_nan=False)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    p1_events, dec_events, dec_bytes, q_events = [], [], [], []
+
+    def step(record: bool):
+        p.write_context()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        p.phase1()
+        e1.record(stream)
+        if record:
+            p1_events.append((e0, e1))
+        q0, q1 = ev(), ev()
+        q0.record(stream)
+        p.query_step()
+        q1.record(stream)
+        if record:
+            q_events.append((q0, q1))
+        d0 = ev()
+        d0.record(stream)
+        for t in range(w.n_decode):
+            row = w.n_query + t
+            kv_len = w.ctx_len + row + 1
+            sa.star_kv_write(p.desc, p.k_cache, p.v_cache, w.ctx_len + row, p.k_tail_rows[row],
+                             p.v_tail_rows[row], 1)
+            n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
+            k0, k1 = ev(), ev()
+            k0.record(stream)
+            sa.star_attn_phase2_partial(p.desc, p.k_cache, p.v_cache, kv_len,
+                                        p.q_tail_rows[row], 1, o_part, lse_part)
+            k1.record(stream)
+            sa.star_attn_lse_merge(p.desc, 1, n_split, o_part, lse_part, o, p.dtype, lse)
+            if record:
+                dec_events.append((k0, k1))
+                dec_bytes.append(decode_bytes(w, kv_len, n_split))
+        d1 = ev()
+        d1.record(stream)
+        return d0, d1
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    dec_loops = []
+    t0 = time.perf_counter()
+    s0 = ev()
+    s0.record(stream)
+    for _ in range(args.steps):
+        dec_loops.append(step(True))
+    s1 = ev()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = s0.elapsed_time(s1)
+    assert torch.isfinite(p.o_ctx.float()).all(), "non-finite phase-1 output"
+
+    p1_ms = float(np.median([a.elapsed_time(b) for a, b in p1_events]))
+    p1_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in p1_events]))
+    q_ms = float(np.median([a.elapsed_time(b) for a, b in q_events]))
+    dec_loop_ms = float(np.median([a.elapsed_time(b) for a, b in dec_loops]))
+    dec_kernel_ms = np.array([a.elapsed_time(b) for a, b in dec_events])
+    ctx_tok_s = w.batch * w.ctx_len / (p1_ms * 1e-3)
+    flops = phase1_flops(w)
+    p1_tflops = flops / (p1_avg_ms * 1e-3) / 1e12
+    dec_gbs = float(np.sum(dec_bytes) / (np.sum(dec_kernel_ms) * 1e-3) / 1e9)
+    step_us = dec_loop_ms * 1e3 / w.n_decode
+
+    kname1 = "attn_wide_kernel<128,phase1>"
+    kname2 = "attn_narrow_kernel<128>"
+    t1, t2 = load_traffic(kname1), load_traffic(kname2)
+    out = {
+        "metric": METRIC,
+        "value": ctx_tok_s,
+        "unit": "ctx tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": max(wall_ms, gpu_ms) / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx_len": w.ctx_len,
+                   "block_len": w.block_len, "anchor_len": w.anchor_len,
+                   "n_query": w.n_query, "n_decode": w.n_decode,
+                   "peaked_k_rows": w.peak_frac, "peak_factor": w.peak_factor},
+        "phase1_ms": p1_ms,
+        "phase1_ctx_tokens_per_s": ctx_tok_s,
+        "query_step_ms": q_ms,
+        "decode_us_per_step": step_us,
+        "decode_us_per_token": step_us / w.batch,
+        "decode_partial_kernel_us": float(np.mean(dec_kernel_ms) * 1e3),
+        "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": t1, "kernel": kname1,
+                     "algorithmic": f"{flops:.4e} FLOP per launch (4*d per visible pair)"},
+        "roofline_phase2": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS, "traffic": t2,
+                            "kernel": kname2,
+                            "algorithmic": "K+V rows [0, kv_len) + q + fp32 partials per launch"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+"""ctypes binding of libstarattn (include/star_attn.h), same names as the C ABI.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of ``libstarattn.so``. Tensor arguments are PyTorch device tensors
+(device memory and streams are PyTorch's); their shapes, dtypes and
+contiguity are checked here so that a wrong buffer raises instead of being
+read out of bounds. Integer arguments are raw device pointers and are passed
+as they are. The stream defaults to torch's current stream.
+
+The library must be built (``python -m long_context_attention_phase1_amd.build``);
+loading fails loudly otherwise, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libstarattn.so")
+
+STAR_OK = 0
+STAR_ERR_INVALID_ARG = -1
+STAR_ERR_SHAPE = -2
+STAR_ERR_DTYPE = -3
+STAR_ERR_UNSUPPORTED = -4
+STAR_ERR_HIP = -5
+STAR_BF16 = 0
+STAR_F32 = 1
+STAR_KV_TILE = 64
+
+EXPORTS = ("star_kv_cache_bytes", "star_kv_write", "star_attn_phase1", "star_attn_phase2_plan",
+           "star_attn_phase2_split_range", "star_attn_phase2_partial", "star_attn_lse_merge",
+           "star_attn_strerror", "star_attn_abi_version")
+
+
+class StarAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {star_attn_strerror(status)}")
+
+
+class StarAttnDesc(ctypes.Structure):
+    """Mirror of ``star_attn_desc``."""
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ctx_len", ctypes.c_int64), ("block_len", ctypes.c_int64),
+                ("anchor_len", ctypes.c_int64), ("tail_cap", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libstarattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m long_context_attention_phase1_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    D = ctypes.POINTER(StarAttnDesc)
+    sig = {
+        "star_kv_cache_bytes": (ctypes.c_size_t, [D]),
+        "star_kv_write": (ctypes.c_int, [D, P, P, I64, P, P, I64, P]),
+        "star_attn_phase1": (ctypes.c_int, [D, P, P, P, P, P]),
+        "star_attn_phase2_plan": (ctypes.c_int, [D, I64, I64, ctypes.POINTER(I32)]),
+        "star_attn_phase2_split_range": (ctypes.c_int, [D, I64, I64, I32, ctypes.POINTER(I64),
+                                                        ctypes.POINTER(I64), ctypes.POINTER(I32)]),
+        "star_attn_phase2_partial": (ctypes.c_int, [D, P, P, I64, P, I64, P, P, P]),
+        "star_attn_lse_merge": (ctypes.c_int, [D, I64, I32, P, P, P, I32, P, P]),
+        "star_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "star_attn_abi_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def make_desc(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ctx_len: int,
+              block_len: int, anchor_len: int, tail_cap: int, dtype: int = STAR_BF16,
+              softmax_scale: float = 0.0) -> StarAttnDesc:
+    return StarAttnDesc(batch, n_q_heads, n_kv_heads, head_dim, ctx_len, block_len, anchor_len,
+                        tail_cap, dtype, softmax_scale)
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream) if not hasattr(stream, "cuda_stream") else stream.cuda_stream
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _elt(desc: StarAttnDesc):
+    torch = _torch()
+    return torch.bfloat16 if desc.dtype == STAR_BF16 else torch.float32
+
+
+def _ptr(x, shape=None, dtype=None, name="buffer") -> Optional[int]:
+    """Device pointer of a tensor (checked) or an integer passed through."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or an int pointer")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{name}: dtype {x.dtype}, expected {dtype}")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {tuple(shape)}")
+    return x.data_ptr()
+
+
+def _cache_ptr(desc, x, name):
+    if isinstance(x, int) or x is None:
+        return x
+    nbytes = star_kv_cache_bytes(desc)
+    if x.numel() * x.element_size() < nbytes:
+        raise ValueError(f"{name}: {x.numel() * x.element_size()} bytes < {nbytes}")
+    return _ptr(x, name=name)
+
+
+def _check(status: int, where: str):
+    if status != STAR_OK:
+        raise StarAttnError(status, where)
+
+
+# ---------------------------------------------------------------- entry points
+
+def star_attn_strerror(status: int) -> str:
+    return load_library().star_attn_strerror(status).decode()
+
+
+def star_attn_abi_version() -> int:
+    return load_library().star_attn_abi_version()
+
+
+def star_kv_cache_bytes(desc: StarAttnDesc) -> int:
+    return load_library().star_kv_cache_bytes(ctypes.byref(desc))
+
+
+def alloc_kv_cache(desc: StarAttnDesc, device="cuda"):
+    """One K or V cache buffer (torch.empty of star_kv_cache_bytes)."""
+    torch = _torch()
+    nbytes = star_kv_cache_bytes(desc)
+    if nbytes == 0:
+        raise StarAttnError(STAR_ERR_INVALID_ARG, "alloc_kv_cache")
+    elt = _elt(desc)
+    return torch.empty(nbytes // torch.tensor([], dtype=elt).element_size(), dtype=elt,
+                       device=device)
+
+
+def star_kv_write(desc, k_cache, v_cache, pos0: int, k_src, v_src, n_tok: int, stream=None):
+    shp = (desc.batch, n_tok, desc.n_kv_heads, desc.head_dim)
+    elt = None if isinstance(k_src, int) else _elt(desc)
+    st = load_library().star_kv_write(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        pos0, _ptr(k_src, shp, elt, "k_src"), _ptr(v_src, shp, elt, "v_src"), n_tok, _stream(stream))
+    _check(st, "star_kv_write")
+
+
+def star_attn_phase1(desc, k_cache, v_cache, q_ctx, o_ctx, stream=None):
+    shp = (desc.batch, desc.ctx_len, desc.n_q_heads, desc.head_dim)
+    elt = None if isinstance(q_ctx, int) else _elt(desc)
+    st = load_library().star_attn_phase1(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        _ptr(q_ctx, shp, elt, "q_ctx"), _ptr(o_ctx, shp, elt, "o_ctx"), _stream(stream))
+    _check(st, "star_attn_phase1")
+
+
+def star_attn_phase2_plan(desc, kv_len: int, n_query: int) -> int:
+    n = ctypes.c_int32(0)
+    _check(load_library().star_attn_phase2_plan(ctypes.byref(desc), kv_len, n_query,
+                                                ctypes.byref(n)), "star_attn_phase2_plan")
+    return n.value
+
+
+def star_attn_phase2_split_range(desc, kv_len: int, n_query: int, split: int) -> Tuple[int, int, int]:
+    lo, hi, host = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(load_library().star_attn_phase2_split_range(
+        ctypes.byref(desc), kv_len, n_query, split, ctypes.byref(lo), ctypes.byref(hi),
+        ctypes.byref(host)), "star_attn_phase2_split_range")
+    return lo.value, hi.value, host.value
+
+
+def star_attn_phase2_partial(desc, k_cache, v_cache, kv_len: int, q, n_query: int, o_part,
+                             lse_part, stream=None):
+    torch = None if isinstance(q, int) else _torch()
+    n_split = star_attn_phase2_plan(desc, kv_len, n_query)
+    shp_q = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    shp_o = (desc.batch, n_query, desc.n_q_heads, n_split, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    st = load_library().star_attn_phase2_partial(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        kv_len, _ptr(q, shp_q, None if torch is None else _elt(desc), "q"), n_query,
+        _ptr(o_part, shp_o, f32, "o_part"), _ptr(lse_part, shp_o[:4], f32, "lse_part"),
+        _stream(stream))
+    _check(st, "star_attn_phase2_partial")
+
+
+def star_attn_lse_merge(desc, n_query: int, n_split: int, o_part, lse_part, o, o_dtype: int,
+                        lse_out=None, stream=None):
+    torch = None if isinstance(o, int) else _torch()
+    shp_o = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    od = None if torch is None else (torch.bfloat16 if o_dtype == STAR_BF16 else torch.float32)
+    st = load_library().star_attn_lse_merge(
+        ctypes.byref(desc), n_query, n_split,
+        _ptr(o_part, shp_o[:3] + (n_split, desc.head_dim), f32, "o_part"),
+        _ptr(lse_part, shp_o[:3] + (n_split,), f32, "lse_part"), _ptr(o, shp_o, od, "o"), o_dtype,
+        _ptr(lse_out, shp_o[:3], f32, "lse_out"), _stream(stream))
+    _check(st, "star_attn_lse_merge")

@@ -1,0 +1,51 @@
+"""Builds libstarattn.so in-tree for gfx950 with hipcc.
+
+``python -m long_context_attention_phase1_amd.build`` (or
+``__graft_entry__.build()``) compiles every source under ``csrc/`` into
+``long_context_attention_phase1_amd/libstarattn.so``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libstarattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+SOURCES = ["star_host.cpp", "star_kernels.hip"]
+
+# Packed fp32 ALU ops are disabled for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def command(out: str = LIB, extra=()) -> list:
+    return ([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+            + DEVICE_FLAGS + list(extra)
+            + ["-I", os.path.join(PKG, "..", "include")]
+            + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out])
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always rebuilds) and return its path."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,187 @@
+// Host runtime of libstarattn: argument validation, the phase-2 split
+// planner and the extern "C" entry points declared in include/star_attn.h.
+// Pure C++ (no HIP calls), so every check here runs without a GPU; the
+// kernel launches live in star_kernels.hip.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "star_internal.hpp"
+
+namespace star {
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+int validate_desc(const star_attn_desc* d, Dims* out) {
+  if (!d) return STAR_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->ctx_len < 1 ||
+      d->block_len < 1 || d->anchor_len < 1 || d->tail_cap < 0)
+    return STAR_ERR_INVALID_ARG;
+  if (!(d->softmax_scale >= 0.0f) || isinf(d->softmax_scale)) return STAR_ERR_INVALID_ARG;
+  if (d->dtype != STAR_BF16 && d->dtype != STAR_F32) return STAR_ERR_DTYPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return STAR_ERR_UNSUPPORTED;
+  if (d->n_q_heads % d->n_kv_heads != 0) return STAR_ERR_SHAPE;
+  if (d->anchor_len > d->block_len) return STAR_ERR_SHAPE;
+  // keep every element index inside int64 and every grid inside 2^31 workgroups
+  const int64_t rows = round_up(d->ctx_len + d->tail_cap, kTile);
+  if (rows > ((int64_t)1 << 40) || (int64_t)d->batch * d->n_q_heads > (1 << 24))
+    return STAR_ERR_SHAPE;
+  if (out) {
+    Dims& o = *out;
+    o.B = d->batch;
+    o.Hq = d->n_q_heads;
+    o.Hkv = d->n_kv_heads;
+    o.G = d->n_q_heads / d->n_kv_heads;
+    o.D = d->head_dim;
+    o.L = d->ctx_len;
+    o.blk = d->block_len;
+    o.anc = d->anchor_len;
+    o.tail_cap = d->tail_cap;
+    o.rows = rows;
+    o.n_blocks = (int32_t)cdiv(d->ctx_len, d->block_len);
+    o.dtype = d->dtype;
+    o.scale = d->softmax_scale == 0.0f ? (float)(1.0 / sqrt((double)d->head_dim))
+                                       : d->softmax_scale;
+    o.scale_log2 = (float)((double)o.scale * 1.4426950408889634);
+    o.HW = (o.G % 4 == 0) ? 4 : (o.G % 2 == 0 ? 2 : 1);
+    o.RW = kWaves / o.HW;
+    o.HQ = o.G / o.HW;
+  }
+  return STAR_OK;
+}
+
+int validate_phase2(const Dims& d, int64_t kv_len, int64_t n_query) {
+  if (n_query < 1) return STAR_ERR_INVALID_ARG;
+  if (kv_len < d.L + 1 || kv_len > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  if (n_query > kv_len - d.L) return STAR_ERR_SHAPE;
+  return STAR_OK;
+}
+
+Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
+  Plan p{};
+  const int64_t cols = n_query * d.G;
+  p.narrow = (d.dtype != STAR_BF16) || cols <= kNarrowCols;
+  p.n_groups = p.narrow ? d.B * d.Hkv : d.B * d.Hkv * d.HQ;
+  p.n_qtiles = p.narrow ? 1 : (int32_t)cdiv(n_query, (int64_t)kColsPerWave * d.RW);
+  int64_t target = kTargetWorkgroups / ((int64_t)p.n_groups * p.n_qtiles);
+  if (target < 1) target = 1;
+  // splits per context block: proportional to the block's share of the cache,
+  // no split shorter than 256 rows
+  int64_t per = (int64_t)llround((double)target * (double)d.blk / (double)kv_len);
+  const int64_t max_per = d.blk / 256;
+  if (per > max_per) per = max_per;
+  if (per <= 1) {
+    p.per_block = 1;
+    p.blk_len = d.blk;
+  } else {
+    p.blk_len = round_up(cdiv(d.blk, per), kTile);
+    p.per_block = (int32_t)cdiv(d.blk, p.blk_len);
+  }
+  const int64_t tail = kv_len - d.L;
+  const int64_t tl_target = p.per_block > 1 ? p.blk_len : (d.blk > 256 ? round_up(d.blk, kTile) : 256);
+  p.tail_splits = (int32_t)cdiv(tail, tl_target);
+  p.tail_len = p.tail_splits == 1 ? tail : round_up(cdiv(tail, p.tail_splits), kTile);
+  p.n_split = d.n_blocks * p.per_block + p.tail_splits;
+  return p;
+}
+
+}  // namespace star
+
+using namespace star;
+
+extern "C" {
+
+size_t star_kv_cache_bytes(const star_attn_desc* desc) {
+  Dims d;
+  if (validate_desc(desc, &d) != STAR_OK) return 0;
+  const size_t elt = d.dtype == STAR_BF16 ? 2 : 4;
+  return (size_t)d.B * d.Hkv * (size_t)d.rows * d.D * elt;
+}
+
+int star_kv_write(const star_attn_desc* desc, void* k_cache, void* v_cache, int64_t pos0,
+                  const void* k_src, const void* v_src, int64_t n_tok, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !k_src || !v_src || n_tok < 1) return STAR_ERR_INVALID_ARG;
+  if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  return launch_kv_write(d, k_cache, v_cache, pos0, k_src, v_src, n_tok, stream);
+}
+
+int star_attn_phase1(const star_attn_desc* desc, const void* k_cache, const void* v_cache,
+                     const void* q_ctx, void* o_ctx, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !q_ctx || !o_ctx) return STAR_ERR_INVALID_ARG;
+  return launch_phase1(d, k_cache, v_cache, q_ctx, o_ctx, stream);
+}
+
+int star_attn_phase2_plan(const star_attn_desc* desc, int64_t kv_len, int64_t n_query,
+                          int32_t* n_split) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!n_split) return STAR_ERR_INVALID_ARG;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  *n_split = make_plan(d, kv_len, n_query).n_split;
+  return STAR_OK;
+}
+
+int star_attn_phase2_split_range(const star_attn_desc* desc, int64_t kv_len, int64_t n_query,
+                                 int32_t split, int64_t* lo, int64_t* hi, int32_t* host) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!lo || !hi || !host) return STAR_ERR_INVALID_ARG;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  if (split < 0 || split >= p.n_split) return STAR_ERR_SHAPE;
+  split_range(d, p, kv_len, split, lo, hi, host);
+  return STAR_OK;
+}
+
+int star_attn_phase2_partial(const star_attn_desc* desc, const void* k_cache, const void* v_cache,
+                             int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                             float* lse_part, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !q || !o_part || !lse_part) return STAR_ERR_INVALID_ARG;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  return launch_phase2_partial(d, p, k_cache, v_cache, kv_len, q, n_query, o_part, lse_part,
+                               stream);
+}
+
+int star_attn_lse_merge(const star_attn_desc* desc, int64_t n_query, int32_t n_split,
+                        const float* o_part, const float* lse_part, void* o, int32_t o_dtype,
+                        float* lse_out, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!o_part || !lse_part || !o || n_query < 1 || n_split < 1) return STAR_ERR_INVALID_ARG;
+  if (o_dtype != STAR_BF16 && o_dtype != STAR_F32) return STAR_ERR_DTYPE;
+  if (n_query > d.tail_cap) return STAR_ERR_SHAPE;
+  return launch_lse_merge(d, n_query, n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
+}
+
+const char* star_attn_strerror(int status) {
+  switch (status) {
+    case STAR_OK: return "success";
+    case STAR_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad scale)";
+    case STAR_ERR_SHAPE: return "inconsistent shape (heads, anchor/block, kv_len, n_query or cache range)";
+    case STAR_ERR_DTYPE: return "unknown dtype";
+    case STAR_ERR_UNSUPPORTED: return "unsupported head_dim (64 or 128)";
+    case STAR_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int star_attn_abi_version(void) { return STAR_ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host runtime (star_host.cpp) and the
+// HIP kernels (star_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/star_attn.h"
+
+namespace star {
+
+constexpr int kTile = STAR_KV_TILE;   // rows of a KV-cache tile
+constexpr int kWaves = 4;             // waves per workgroup of the MFMA kernels
+constexpr int kColsPerWave = 64;      // query columns (row, head pairs) per wave
+constexpr int kNarrowCols = 32;       // columns of the single-tile decode kernel
+constexpr int kTargetWorkgroups = 2048;  // phase-2 split planner target (8 per CU)
+
+// Everything derived from a validated descriptor.
+struct Dims {
+  int32_t B, Hq, Hkv, G, D;
+  int64_t L, blk, anc, tail_cap, rows;  // rows: cache rows per (seq, kv head)
+  int32_t n_blocks;
+  int32_t dtype;
+  float scale;      // softmax scale
+  float scale_log2; // scale * log2(e)
+  // MFMA kernels: heads per workgroup (HW), 64-row sub-tiles per workgroup
+  // (RW = 4 / HW), head sub-groups per kv head (HQ = G / HW).
+  int32_t HW, RW, HQ;
+};
+
+// Phase-2 split plan: every split lies inside one host's share.
+struct Plan {
+  int32_t narrow;         // 1: single-column-tile decode kernel, 0: wide kernel
+  int32_t per_block;      // splits per context block
+  int64_t blk_len;        // rows per block split
+  int32_t tail_splits;    // splits of the tail [L, kv_len)
+  int64_t tail_len;       // rows per tail split
+  int32_t n_split;
+  int32_t n_groups;       // workgroup groups (sequence, kv head[, head sub-group])
+  int32_t n_qtiles;       // query-row tiles (wide kernel)
+};
+
+int validate_desc(const star_attn_desc* d, Dims* out);
+int validate_phase2(const Dims& d, int64_t kv_len, int64_t n_query);
+Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query);
+
+#if defined(__HIPCC__)
+#define STAR_HD __host__ __device__
+#else
+#define STAR_HD
+#endif
+
+// Split sigma of a plan -> rows [lo, hi) (lo == hi: empty) and host id
+// (context block index, or n_blocks for the tail).
+STAR_HD static inline void split_rows(int64_t L, int64_t blk, int32_t n_blocks, int32_t per_block,
+                                      int64_t blk_len, int64_t tail_len, int64_t kv_len,
+                                      int32_t sigma, int64_t* lo, int64_t* hi, int32_t* host) {
+  const int64_t nb = (int64_t)n_blocks * per_block;
+  if (sigma < nb) {
+    const int64_t i = sigma / per_block, j = sigma % per_block;
+    const int64_t bend = (i + 1) * blk < L ? (i + 1) * blk : L;
+    int64_t a = i * blk + j * blk_len, b = a + blk_len;
+    if (b > bend) b = bend;
+    if (a > b) a = b;
+    *lo = a; *hi = b; *host = (int32_t)i;
+  } else {
+    const int64_t t = sigma - nb;
+    int64_t a = L + t * tail_len, b = a + tail_len;
+    if (b > kv_len) b = kv_len;
+    if (a > b) a = b;
+    *lo = a; *hi = b; *host = n_blocks;
+  }
+}
+
+static inline void split_range(const Dims& d, const Plan& p, int64_t kv_len, int32_t sigma,
+                               int64_t* lo, int64_t* hi, int32_t* host) {
+  split_rows(d.L, d.blk, d.n_blocks, p.per_block, p.blk_len, p.tail_len, kv_len, sigma, lo, hi,
+             host);
+}
+
+// Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
+int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
+                    const void* vs, int64_t n_tok, void* stream);
+int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
+                  void* stream);
+int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
+                          int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                          float* lse_part, void* stream);
+int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const float* o_part,
+                     const float* lse_part, void* o, int32_t o_dtype, float* lse_out,
+                     void* stream);
+
+}  // namespace star

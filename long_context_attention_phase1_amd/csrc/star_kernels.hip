@@ -1,0 +1,965 @@
+// HIP kernels of libstarattn for gfx950 (CDNA4, 64-wide wavefronts).
+//
+//   kv_write_kernel     token-major K/V rows -> cache rows (K row-major, V as
+//                       transposed 64-row tiles)
+//   attn_wide_kernel    flash-style bf16 MFMA tile loop shared by phase 1
+//                       (anchor pass + local causal pass, normalised bf16
+//                       output) and by phase-2 partials with many query rows
+//   attn_narrow_kernel  split-KV decode partials (<= 32 query columns)
+//   attn_f32_kernel     fp32 path (VALU) for both phases
+//   lse_merge_kernel    exact softmax renormalisation of the partials
+//
+// Method: Star Attention (hotaipapers.com summary page, podcast transcript,
+// Phase 1 and Phase 2 descriptions; paperhub.cn rebuttal, reply to reviewer
+// EMsM point 5). See include/star_attn.h for the exact definitions.
+//
+// MFMA formulation. Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: the A operand is a 32-key slice of the K tile
+// (from LDS), the B operand is 32 query columns (registers, loaded once).
+// The accumulator then holds, per lane, one query column and 16 keys, so the
+// softmax max/sum over keys is lane-local plus one exchange with lane ^ 32.
+// The same registers, rounded to bf16, are the B operand of O^T += V^T P^T,
+// whose A operand is read from the transposed V tile. Key slots of the K tile
+// are permuted (bits 2 and 3 of the slot swapped) so that each lane's
+// accumulator keys are 8 consecutive keys, i.e. one 16-byte read of V^T.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "star_internal.hpp"
+
+namespace star {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kMinit = -1.0e30f;  // running-max start: finite, below any score
+
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// K-tile slot -> key offset inside a 32-key slice (bits 2 and 3 swapped).
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+// Key (0..31 inside a slice) held in accumulator element i by lane half g.
+__device__ __forceinline__ int acc_key(int i, int g) { return ((i >> 3) << 4) + (g << 3) + (i & 7); }
+
+// LDS byte offset of logical 16-byte chunk c of K slot `slot` (XOR swizzle).
+template <int D>
+__device__ __forceinline__ uint32_t k_off(int slot, int c) {
+  return (uint32_t)(slot * (D * 2) + ((c ^ (slot & (D / 8 - 1))) << 4));
+}
+// LDS byte offset of key chunk kc (8 keys) of row e of a transposed V tile.
+__device__ __forceinline__ uint32_t v_off(int e, int kc) {
+  return (uint32_t)(e * 128 + ((kc ^ (e & 7)) << 4));
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 lds16(const char* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void sts16(char* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Zero the bf16 elements of an 8-key chunk whose key lies outside [lo, hi).
+__device__ __forceinline__ u32x4 mask_chunk(u32x4 x, int64_t k0, int64_t lo, int64_t hi) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int64_t ka = k0 + 2 * w, kb = ka + 1;
+    uint32_t m = 0;
+    if (ka >= lo && ka < hi) m |= 0x0000FFFFu;
+    if (kb >= lo && kb < hi) m |= 0xFFFF0000u;
+    x[w] &= m;
+  }
+  return x;
+}
+
+// Load one 16-byte chunk of a transposed V tile, zeroing keys outside [lo, hi).
+__device__ __forceinline__ u32x4 load_v_chunk(const uint16_t* p, int64_t k0, int64_t lo,
+                                              int64_t hi) {
+  if (k0 >= lo && k0 + 8 <= hi) return ld16(p);
+  if (k0 + 8 <= lo || k0 >= hi) return u32x4{0, 0, 0, 0};
+  return mask_chunk(ld16(p), k0, lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// kv_write
+// ---------------------------------------------------------------------------
+struct KvArgs {
+  void* kc;
+  void* vc;
+  const void* ks;
+  const void* vs;
+  int64_t pos0, n_tok, rows, t0;
+  int32_t Hkv, nt;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
+  constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / VEC;              // chunks per row
+  __shared__ __attribute__((aligned(16))) T vsm[64][D + VEC];
+  const int tid = threadIdx.x;
+  const int64_t tile = a.t0 + blockIdx.x % a.nt;
+  const int sg = blockIdx.x / a.nt;
+  const int g = sg % a.Hkv, s = sg / a.Hkv;
+  const int64_t r0 = tile * 64;
+  const int64_t r_lo = a.pos0 > r0 ? a.pos0 : r0;
+  const int64_t r_hi = (a.pos0 + a.n_tok) < (r0 + 64) ? (a.pos0 + a.n_tok) : (r0 + 64);
+  const int64_t head_row0 = ((int64_t)s * a.Hkv + g) * a.rows;
+  T* kc = (T*)a.kc;
+  T* vc = (T*)a.vc;
+  const T* ks = (const T*)a.ks;
+  const T* vs = (const T*)a.vs;
+  for (int u = tid; u < 64 * CPR; u += 256) {
+    const int rr = u / CPR, c = u % CPR;
+    const int64_t r = r0 + rr;
+    if (r >= r_lo && r < r_hi) {
+      const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
+      *(u32x4*)(kc + (head_row0 + r) * D + c * VEC) = *(const u32x4*)(ks + src);
+      *(u32x4*)(&vsm[rr][c * VEC]) = *(const u32x4*)(vs + src);
+    }
+  }
+  __syncthreads();
+  T* vt = vc + (head_row0 + r0) * D;  // transposed tile: element (e, kk) at e*64 + kk
+  if (r_lo == r0 && r_hi == r0 + 64) {
+    constexpr int KC = 64 / VEC;
+    for (int u = tid; u < D * KC; u += 256) {
+      const int e = u / KC, kc0 = (u % KC) * VEC;
+      T tmp[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) tmp[j] = vsm[kc0 + j][e];
+      *(u32x4*)(vt + e * 64 + kc0) = *(const u32x4*)tmp;
+    }
+  } else {
+    for (int u = tid; u < D * 64; u += 256) {
+      const int e = u / 64, kk = u % 64;
+      const int64_t r = r0 + kk;
+      if (r >= r_lo && r < r_hi) vt[e * 64 + kk] = vsm[kk][e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide kernel: 4 waves x 64 query columns share 64-key K / V^T tiles in LDS.
+// ---------------------------------------------------------------------------
+struct WideArgs {
+  const uint16_t* k;  // cache K (row-major rows)
+  const uint16_t* v;  // cache V (transposed 64-row tiles)
+  const uint16_t* q;  // [B][q_tokens][Hq][D]
+  uint16_t* o;        // phase 1: [B][L][Hq][D]
+  float* o_part;      // phase 2: [B][n_query][Hq][n_split][D]
+  float* lse_part;    // phase 2: [B][n_query][Hq][n_split]
+  int64_t rows;       // cache rows per (seq, kv head)
+  int64_t q_tokens;   // tokens per sequence in q (ctx_len or n_query)
+  int64_t L, blk, anc, kv_len;
+  int64_t blk_len, tail_len;  // split plan
+  int32_t per_block, n_split, n_blocks;
+  int32_t Hq, Hkv, G, HW, HQ, NG, NRT;  // NRT: row tiles (phase 1) / query tiles (phase 2)
+  int32_t BM;                           // rows per workgroup = 64 * (4 / HW)
+  float scale, c2;                      // softmax scale and scale*log2(e)
+};
+
+template <int D>
+struct WideTile {
+  static constexpr int CH = D / 8;          // 16-byte chunks per K row
+  static constexpr int KPT = 64 * CH / 256; // K chunks per thread
+  static constexpr int VPT = D * 8 / 256;   // V chunks per thread
+  static constexpr int KBYTES = 64 * D * 2;
+  static constexpr int STAGE = 2 * KBYTES;  // K tile + V^T tile
+  u32x4 kr[KPT], vr[VPT];
+
+  __device__ __forceinline__ void load(const uint16_t* K, const uint16_t* V, int64_t kbase,
+                                       int64_t lo, int64_t hi, int tid) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + 256 * i, slot = u / CH, c = u % CH;
+      const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
+      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + 256 * i, e = u >> 3, kc = u & 7;
+      vr[i] = load_v_chunk(V + kbase * D + e * 64 + kc * 8, kbase + kc * 8, lo, hi);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + 256 * i;
+      sts16(lds + k_off<D>(u / CH, u % CH), kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + 256 * i;
+      sts16(lds + KBYTES + v_off(u >> 3, u & 7), vr[i]);
+    }
+  }
+};
+
+// Online-softmax update of one query-column tile from raw scores s[kt]
+// (NKT 32-key slices); returns the packed bf16 P operands.
+template <int NKT, int DT>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[NKT], float& m, float& l,
+                                               f32x16 (&o)[DT], u32x4 (&p)[NKT][2], float c2) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m, mx);
+  const float alpha = fast_exp2((m - m_new) * c2);
+  const float mc = m_new * c2;
+  float rs = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = fast_exp2(fmaf(s[kt][i], c2, -mc));
+      s[kt][i] = e;
+      rs += e;
+    }
+  l = l * alpha + rs;
+  m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int b = kb * 8;
+      p[kt][kb] = u32x4{pack_bf16(s[kt][b + 0], s[kt][b + 1]), pack_bf16(s[kt][b + 2], s[kt][b + 3]),
+                        pack_bf16(s[kt][b + 4], s[kt][b + 5]), pack_bf16(s[kt][b + 6], s[kt][b + 7])};
+    }
+}
+
+template <int D, bool PHASE1>
+__global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
+  constexpr int KS = D / 16;  // k-steps over the head dimension
+  constexpr int DT = D / 32;  // 32-row tiles of the output dimension
+  using Tile = WideTile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Tile::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // ---- which (group, work item) this workgroup is
+  const int64_t bid = blockIdx.x;
+  const int gidx = (int)(bid % a.NG);
+  const int64_t work = bid / a.NG;
+  const int hq = gidx % a.HQ, t2 = gidx / a.HQ;
+  const int kvh = t2 % a.Hkv, s = t2 / a.Hkv;
+  const int hw = w % a.HW, rw = w / a.HW;
+  const int head = kvh * a.G + hq * a.HW + hw;
+
+  int64_t row0, row_end, loA = 0, hiA = 0, loB, hiB, pos_off;
+  int32_t sigma = 0;
+  if (PHASE1) {
+    // heaviest tiles first: anchored blocks by descending row tile, then block 0
+    const int64_t n1 = (int64_t)(a.n_blocks - 1) * a.NRT;
+    int64_t i, rt;
+    if (work < n1) {
+      rt = a.NRT - 1 - work / (a.n_blocks - 1);
+      i = 1 + work % (a.n_blocks - 1);
+    } else {
+      rt = a.NRT - 1 - (work - n1);
+      i = 0;
+    }
+    row0 = i * a.blk + rt * a.BM;
+    row_end = (i + 1) * a.blk < a.L ? (i + 1) * a.blk : a.L;
+    if (row0 >= row_end) return;
+    if (i > 0) hiA = a.anc;
+    loB = i * a.blk;
+    hiB = row0 + a.BM < row_end ? row0 + a.BM : row_end;
+    pos_off = 0;
+  } else {
+    const int64_t qrt = work % a.NRT;
+    sigma = (int32_t)(work / a.NRT);
+    row0 = qrt * a.BM;
+    row_end = a.q_tokens;
+    if (row0 >= row_end) return;
+    int32_t host;
+    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &loB,
+               &hiB, &host);
+    pos_off = a.kv_len - a.q_tokens;
+  }
+  const int64_t wrow0 = row0 + rw * 64;  // this wave's first query row
+  const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
+  const uint16_t* K = a.k + head_row0 * D;
+  const uint16_t* V = a.v + head_row0 * D;
+
+  // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g
+  u32x4 qop[2][KS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t r = wrow0 + 32 * qt + l32;
+    const bool ok = r < row_end;
+    const uint16_t* qp = a.q + (((int64_t)s * a.q_tokens + (ok ? r : 0)) * a.Hq + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[qt][ks] = ok ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 oacc[2][DT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x16{};
+  float m[2] = {kMinit, kMinit}, l[2] = {0.0f, 0.0f};
+
+  const int nA = hiA > loA ? (int)cdiv64(hiA, 64) : 0;
+  const int64_t kb0 = (loB / 64) * 64;
+  const int nB = hiB > loB ? (int)cdiv64(hiB - kb0, 64) : 0;
+  const int nT = nA + nB;
+  const int64_t min_pos = row0 + pos_off;
+
+  if (nT > 0) {
+    Tile st;
+    {
+      const bool inA = 0 < nA;
+      st.load(K, V, inA ? 0 : kb0, inA ? loA : loB, inA ? hiA : hiB, tid);
+      st.store(smem, tid);
+    }
+    __syncthreads();
+    for (int t = 0; t < nT; ++t) {
+      if (t + 1 < nT) {
+        const bool inA = t + 1 < nA;
+        st.load(K, V, inA ? (int64_t)(t + 1) * 64 : kb0 + (int64_t)(t + 1 - nA) * 64,
+                inA ? loA : loB, inA ? hiA : hiB, tid);
+      }
+      const char* buf = smem + (t & 1) * Tile::STAGE;
+      const bool inA = t < nA;
+      const int64_t kbase = inA ? (int64_t)t * 64 : kb0 + (int64_t)(t - nA) * 64;
+      const int64_t lo = inA ? loA : loB, hi = inA ? hiA : hiB;
+      const bool causal = !inA;
+      const bool edge = kbase < lo || kbase + 64 > hi || (causal && kbase + 63 > min_pos);
+
+      f32x16 sacc[2][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[qt][kt] = f32x16{};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kop = lds16(buf + k_off<D>(32 * kt + l32, 2 * ks + g));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) sacc[qt][kt] = mfma_bf16(kop, qop[qt][ks], sacc[qt][kt]);
+        }
+      if (edge) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int64_t pos = wrow0 + 32 * qt + l32 + pos_off;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int64_t key = kbase + 32 * kt + acc_key(i, g);
+              if (key < lo || key >= hi || (causal && key > pos)) sacc[qt][kt][i] = -INFINITY;
+            }
+        }
+      }
+      u32x4 p[2][2][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) softmax_update<2, DT>(sacc[qt], m[qt], l[qt], oacc[qt], p[qt], a.c2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 vop = lds16(buf + Tile::KBYTES + v_off(32 * dt + l32, 4 * kt + 2 * kb + g));
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) oacc[qt][dt] = mfma_bf16(vop, p[qt][kt][kb], oacc[qt][dt]);
+          }
+      if (t + 1 < nT) st.store(smem + ((t + 1) & 1) * Tile::STAGE, tid);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: accumulator element i of tile dt is dimension 32*dt + 8*(i/4) + 4*g + i%4
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+    const int64_t r = wrow0 + 32 * qt + l32;
+    if (r >= row_end) continue;
+    if (PHASE1) {
+      const float inv = 1.0f / lt;
+      uint16_t* op = a.o + (((int64_t)s * a.L + r) * a.Hq + head) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x16& x = oacc[qt][dt];
+          uint2 v2;
+          v2.x = pack_bf16(x[4 * j4 + 0] * inv, x[4 * j4 + 1] * inv);
+          v2.y = pack_bf16(x[4 * j4 + 2] * inv, x[4 * j4 + 3] * inv);
+          *(uint2*)(op + 32 * dt + 8 * j4 + 4 * g) = v2;
+        }
+    } else {
+      const bool any = lt > 0.0f;
+      const float inv = any ? 1.0f / lt : 0.0f;
+      const int64_t base = (((int64_t)s * a.q_tokens + r) * a.Hq + head) * a.n_split + sigma;
+      float* op = a.o_part + base * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x16& x = oacc[qt][dt];
+          *(f32x4*)(op + 32 * dt + 8 * j4 + 4 * g) =
+              f32x4{x[4 * j4] * inv, x[4 * j4 + 1] * inv, x[4 * j4 + 2] * inv, x[4 * j4 + 3] * inv};
+        }
+      if (g == 0) a.lse_part[base] = any ? m[qt] * a.scale + logf(lt) : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Narrow kernel (decode): one 32-column tile of (query, head-in-group) pairs
+// per (sequence, kv head, split). Stages of 128 keys; wave w owns keys
+// [32w, 32w + 32) of each stage with its own softmax state; the four states
+// are merged through LDS at the end.
+// ---------------------------------------------------------------------------
+struct NarrowArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q;  // [B][n_query][Hq][D]
+  float* o_part;
+  float* lse_part;
+  int64_t rows, L, blk, kv_len, n_query;
+  int64_t blk_len, tail_len;
+  int32_t per_block, n_split, n_blocks;
+  int32_t Hq, Hkv, G, NG;
+  float scale, c2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
+  constexpr int KBYTES = 128 * D * 2;     // 128 K rows
+  constexpr int VTBYTES = D * 128;        // one transposed 64-key V tile
+  constexpr int KPT = 128 * CH / 256, VPT = 2 * D * 8 / 256;
+  constexpr int SMEM = KBYTES + 2 * VTBYTES;
+  static_assert(SMEM >= 4 * 32 * D * 4, "merge area must fit");
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ float msm[4][32], lsm[4][32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int gidx = (int)(blockIdx.x % a.NG);
+  const int32_t sigma = (int32_t)(blockIdx.x / a.NG);
+  const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
+  int64_t lo, hi;
+  int32_t host;
+  split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo, &hi,
+             &host);
+  const int64_t pos0 = a.kv_len - a.n_query;
+  const int ncols = (int)(a.n_query * a.G);
+  // column l32 -> (query j, head)
+  const int cj = l32 / a.G, ch = kvh * a.G + l32 % a.G;
+  const bool cvalid = l32 < ncols;
+  const int64_t cpos = pos0 + cj;
+
+  const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
+  const uint16_t* K = a.k + head_row0 * D;
+  const uint16_t* V = a.v + head_row0 * D;
+
+  u32x4 qop[KS];
+  {
+    const uint16_t* qp = a.q + (((int64_t)s * a.n_query + (cvalid ? cj : 0)) * a.Hq + ch) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = cvalid ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+  }
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m = kMinit, l = 0.0f;
+
+  const int64_t kb0 = (lo / 64) * 64;
+  const int nS = hi > lo ? (int)cdiv64(hi - kb0, 128) : 0;
+  u32x4 kr[KPT], vr[VPT];
+  auto load = [&](int64_t kbase) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + 256 * i, slot = u / CH, c = u % CH;
+      const int64_t key = kbase + (slot & ~31) + swap23(slot & 31);
+      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + 256 * i, vt = u / (D * 8), rem = u % (D * 8), e = rem >> 3, kc = rem & 7;
+      const int64_t tb = kbase + 64 * vt;
+      vr[i] = load_v_chunk(V + tb * D + e * 64 + kc * 8, tb + kc * 8, lo, hi);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + 256 * i;
+      sts16(smem + k_off<D>(u / CH, u % CH), kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + 256 * i, vt = u / (D * 8), rem = u % (D * 8);
+      sts16(smem + KBYTES + vt * VTBYTES + v_off(rem >> 3, rem & 7), vr[i]);
+    }
+  };
+
+  if (nS > 0) {
+    load(kb0);
+    store();
+    __syncthreads();
+    for (int t = 0; t < nS; ++t) {
+      const int64_t kbase = kb0 + (int64_t)t * 128;
+      if (t + 1 < nS) load(kbase + 128);
+      const int64_t wk = kbase + 32 * w;  // first key of this wave's slice
+      if (wk < hi && wk + 32 > lo) {
+        f32x16 sacc[1] = {f32x16{}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[0] = mfma_bf16(lds16(smem + k_off<D>(32 * w + l32, 2 * ks + g)), qop[ks], sacc[0]);
+        if (wk < lo || wk + 32 > hi || wk + 31 > pos0 || !cvalid) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int64_t key = wk + acc_key(i, g);
+            if (key < lo || key >= hi || key > cpos || !cvalid) sacc[0][i] = -INFINITY;
+          }
+        }
+        u32x4 p[1][2];
+        softmax_update<1, DT>(sacc, m, l, oacc, p, a.c2);
+        const char* vbase = smem + KBYTES + (w >> 1) * VTBYTES;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            oacc[dt] = mfma_bf16(lds16(vbase + v_off(32 * dt + l32, 4 * (w & 1) + 2 * kb + g)),
+                                 p[0][kb], oacc[dt]);
+      }
+      __syncthreads();
+      if (t + 1 < nS) {
+        store();
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- merge the four waves' (m, l, O) and write the split's partial
+  const float lw = l + __shfl_xor(l, 32, 64);
+  if (g == 0) {
+    msm[w][l32] = m;
+    lsm[w][l32] = lw;
+  }
+  float* osm = (float*)smem;  // [4][32][D]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oacc[dt][i];
+  __syncthreads();
+  for (int idx = tid; idx < 32 * D; idx += 256) {
+    const int c = idx / D, e = idx % D;
+    if (c >= ncols) continue;
+    float M = msm[0][c];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, msm[ww][c]);
+    float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = fast_exp2((msm[ww][c] - M) * a.c2);
+      Ls += f * lsm[ww][c];
+      O += f * osm[(ww * 32 + c) * D + e];
+    }
+    const int j = c / a.G, h = kvh * a.G + c % a.G;
+    const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sigma;
+    const bool any = Ls > 0.0f;
+    a.o_part[base * D + e] = any ? O / Ls : 0.0f;
+    if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one wave per (query column[, split]); lanes over keys for the
+// scores, lanes over dimensions for the output. Plain VALU arithmetic.
+// ---------------------------------------------------------------------------
+struct F32Args {
+  const float* k;
+  const float* v;
+  const float* q;
+  float* o;
+  float* o_part;
+  float* lse_part;
+  int64_t rows, q_tokens, L, blk, anc, kv_len, n_cols;
+  int64_t blk_len, tail_len;
+  int32_t per_block, n_split, n_blocks;
+  int32_t Hq, Hkv, G;
+  float scale;
+};
+
+template <int D, bool PHASE1>
+__global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
+  constexpr int E = D / 64;  // output dimensions per lane
+  __shared__ float qsm[4][D];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + w;
+  if (wid >= a.n_cols) return;
+  int64_t s, r, h, sigma = 0, pos;
+  int64_t loA = 0, hiA = 0, loB, hiB;
+  if (PHASE1) {
+    h = wid % a.Hq;
+    const int64_t t = wid / a.Hq;
+    r = t % a.L;
+    s = t / a.L;
+    const int64_t i = r / a.blk;
+    if (i > 0) hiA = a.anc;
+    loB = i * a.blk;
+    hiB = r + 1;
+    pos = r;
+  } else {
+    sigma = wid % a.n_split;
+    int64_t t = wid / a.n_split;
+    h = t % a.Hq;
+    t /= a.Hq;
+    r = t % a.q_tokens;
+    s = t / a.q_tokens;
+    int32_t host;
+    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len,
+               (int32_t)sigma, &loB, &hiB, &host);
+    pos = a.kv_len - a.q_tokens + r;
+    if (hiB > pos + 1) hiB = pos + 1;
+  }
+  const int64_t kvh = h / a.G;
+  const int64_t head_row0 = (s * a.Hkv + kvh) * a.rows;
+  const float* K = a.k + head_row0 * D;
+  const float* V = a.v + head_row0 * D;
+  const float* qp = a.q + ((s * a.q_tokens + r) * a.Hq + h) * D;
+  for (int e = lane; e < D; e += 64) qsm[w][e] = qp[e];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+
+  float m = kMinit, l = 0.0f, o[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) o[j] = 0.0f;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t lo = pass == 0 ? loA : loB, hi = pass == 0 ? hiA : hiB;
+    for (int64_t base = lo; base < hi; base += 64) {
+      const int64_t key = base + lane;
+      const bool ok = key < hi;
+      float sc = -INFINITY;
+      if (ok) {
+        float dot = 0.0f;
+        for (int e = 0; e < D; ++e) dot = fmaf(qsm[w][e], K[key * D + e], dot);
+        sc = dot * a.scale;
+      }
+      const float m_new = fmaxf(m, wave_max(sc));
+      const float alpha = expf(m - m_new);
+      const float p = ok ? expf(sc - m_new) : 0.0f;
+      l = l * alpha + wave_sum(p);
+#pragma unroll
+      for (int j = 0; j < E; ++j) o[j] *= alpha;
+      m = m_new;
+      const int64_t cnt = hi - base < 64 ? hi - base : 64;
+      for (int kk = 0; kk < cnt; ++kk) {
+        const float pk = __shfl(p, kk, 64);
+        const int64_t kr = base + kk;
+        const float* vt = V + (kr / 64) * 64 * D + (kr % 64);
+#pragma unroll
+        for (int j = 0; j < E; ++j) o[j] = fmaf(pk, vt[(lane + 64 * j) * 64], o[j]);
+      }
+    }
+  }
+  if (PHASE1) {
+    float* op = a.o + ((s * a.L + r) * a.Hq + h) * D;
+#pragma unroll
+    for (int j = 0; j < E; ++j) op[lane + 64 * j] = o[j] / l;
+  } else {
+    const int64_t b = ((s * a.q_tokens + r) * a.Hq + h) * a.n_split + sigma;
+    const bool any = l > 0.0f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) a.o_part[b * D + lane + 64 * j] = any ? o[j] / l : 0.0f;
+    if (lane == 0) a.lse_part[b] = any ? m + logf(l) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LSE merge: one workgroup per (sequence, query, head) row.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse_out;
+  int32_t n_split, o_f32;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
+  constexpr int NQ = D / 4;       // threads per split (4 dims each)
+  constexpr int NSG = 256 / NQ;   // splits handled in parallel
+  __shared__ float red[4];
+  __shared__ f32x4 accs[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* lp = a.lse_part + row * a.n_split;
+  const float* op = a.o_part + row * a.n_split * D;
+
+  float mx = -INFINITY;
+  for (int i = tid; i < a.n_split; i += 256) mx = fmaxf(mx, lp[i]);
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const bool empty = M == -INFINITY;
+  float z = 0.0f;
+  if (!empty)
+    for (int i = tid; i < a.n_split; i += 256) z += expf(lp[i] - M);
+  z = wave_sum(z);
+  if (lane == 0) red[w] = z;
+  __syncthreads();
+  const float Z = red[0] + red[1] + red[2] + red[3];
+
+  const int sg = tid / NQ, dq = tid % NQ;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!empty) {
+    for (int i = sg; i < a.n_split; i += NSG) {
+      const float wgt = expf(lp[i] - M);
+      if (wgt > 0.0f) acc += wgt * *(const f32x4*)(op + (int64_t)i * D + 4 * dq);
+    }
+  }
+  accs[tid] = acc;
+  __syncthreads();
+  if (sg == 0) {
+    f32x4 sum = accs[dq];
+#pragma unroll
+    for (int k = 1; k < NSG; ++k) sum += accs[k * NQ + dq];
+    const float inv = empty ? 0.0f : 1.0f / Z;
+    sum *= inv;
+    if (a.o_f32) {
+      *(f32x4*)((float*)a.o + row * D + 4 * dq) = sum;
+    } else {
+      uint2 v2;
+      v2.x = pack_bf16(sum[0], sum[1]);
+      v2.y = pack_bf16(sum[2], sum[3]);
+      *(uint2*)((uint16_t*)a.o + row * D + 4 * dq) = v2;
+    }
+    if (dq == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : M + logf(Z);
+  }
+}
+
+int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
+                    const void* vs, int64_t n_tok, void* stream) {
+  KvArgs a;
+  a.kc = kc;
+  a.vc = vc;
+  a.ks = ks;
+  a.vs = vs;
+  a.pos0 = pos0;
+  a.n_tok = n_tok;
+  a.rows = d.rows;
+  a.t0 = pos0 / 64;
+  a.nt = (int32_t)((pos0 + n_tok - 1) / 64 - a.t0 + 1);
+  a.Hkv = d.Hkv;
+  const dim3 grid((unsigned)((int64_t)a.nt * d.B * d.Hkv));
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == STAR_BF16) {
+    if (d.D == 128) hipLaunchKernelGGL((kv_write_kernel<uint16_t, 128>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((kv_write_kernel<uint16_t, 64>), grid, dim3(256), 0, st, a);
+  } else {
+    if (d.D == 128) hipLaunchKernelGGL((kv_write_kernel<float, 128>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((kv_write_kernel<float, 64>), grid, dim3(256), 0, st, a);
+  }
+  return check_launch();
+}
+
+static F32Args f32_args(const Dims& d, const void* kc, const void* vc, const void* q) {
+  F32Args a{};
+  a.k = (const float*)kc;
+  a.v = (const float*)vc;
+  a.q = (const float*)q;
+  a.rows = d.rows;
+  a.L = d.L;
+  a.blk = d.blk;
+  a.anc = d.anc;
+  a.n_blocks = d.n_blocks;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.scale = d.scale;
+  return a;
+}
+
+int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
+                  void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == STAR_F32) {
+    F32Args a = f32_args(d, kc, vc, q);
+    a.o = (float*)o;
+    a.q_tokens = d.L;
+    a.n_cols = (int64_t)d.B * d.L * d.Hq;
+    const dim3 grid((unsigned)((a.n_cols + 3) / 4));
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, dim3(256), 0, st, a);
+    return check_launch();
+  }
+  WideArgs a{};
+  a.k = (const uint16_t*)kc;
+  a.v = (const uint16_t*)vc;
+  a.q = (const uint16_t*)q;
+  a.o = (uint16_t*)o;
+  a.rows = d.rows;
+  a.q_tokens = d.L;
+  a.L = d.L;
+  a.blk = d.blk;
+  a.anc = d.anc;
+  a.n_blocks = d.n_blocks;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.HW = d.HW;
+  a.HQ = d.HQ;
+  a.BM = kColsPerWave * d.RW;
+  a.NG = d.B * d.Hkv * d.HQ;
+  a.NRT = (int32_t)((d.blk + a.BM - 1) / a.BM);
+  a.scale = d.scale;
+  a.c2 = d.scale_log2;
+  const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
+  const dim3 grid((unsigned)nwg);
+  if (d.D == 128) hipLaunchKernelGGL((attn_wide_kernel<128, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_wide_kernel<64, true>), grid, dim3(256), 0, st, a);
+  return check_launch();
+}
+
+int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
+                          int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                          float* lse_part, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == STAR_F32) {
+    F32Args a = f32_args(d, kc, vc, q);
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.q_tokens = n_query;
+    a.kv_len = kv_len;
+    a.blk_len = p.blk_len;
+    a.tail_len = p.tail_len;
+    a.per_block = p.per_block;
+    a.n_split = p.n_split;
+    a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
+    const dim3 grid((unsigned)((a.n_cols + 3) / 4));
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(256), 0, st, a);
+    return check_launch();
+  }
+  if (p.narrow) {
+    NarrowArgs a{};
+    a.k = (const uint16_t*)kc;
+    a.v = (const uint16_t*)vc;
+    a.q = (const uint16_t*)q;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.rows = d.rows;
+    a.L = d.L;
+    a.blk = d.blk;
+    a.kv_len = kv_len;
+    a.n_query = n_query;
+    a.blk_len = p.blk_len;
+    a.tail_len = p.tail_len;
+    a.per_block = p.per_block;
+    a.n_split = p.n_split;
+    a.n_blocks = d.n_blocks;
+    a.Hq = d.Hq;
+    a.Hkv = d.Hkv;
+    a.G = d.G;
+    a.NG = d.B * d.Hkv;
+    a.scale = d.scale;
+    a.c2 = d.scale_log2;
+    const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
+    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_narrow_kernel<64>), grid, dim3(256), 0, st, a);
+    return check_launch();
+  }
+  WideArgs a{};
+  a.k = (const uint16_t*)kc;
+  a.v = (const uint16_t*)vc;
+  a.q = (const uint16_t*)q;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.rows = d.rows;
+  a.q_tokens = n_query;
+  a.L = d.L;
+  a.blk = d.blk;
+  a.anc = d.anc;
+  a.kv_len = kv_len;
+  a.blk_len = p.blk_len;
+  a.tail_len = p.tail_len;
+  a.per_block = p.per_block;
+  a.n_split = p.n_split;
+  a.n_blocks = d.n_blocks;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.HW = d.HW;
+  a.HQ = d.HQ;
+  a.BM = kColsPerWave * d.RW;
+  a.NG = p.n_groups;
+  a.NRT = p.n_qtiles;
+  a.scale = d.scale;
+  a.c2 = d.scale_log2;
+  const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
+  if (d.D == 128) hipLaunchKernelGGL((attn_wide_kernel<128, false>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_wide_kernel<64, false>), grid, dim3(256), 0, st, a);
+  return check_launch();
+}
+
+int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const float* o_part,
+                     const float* lse_part, void* o, int32_t o_dtype, float* lse_out,
+                     void* stream) {
+  MergeArgs a;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.o = o;
+  a.lse_out = lse_out;
+  a.n_split = n_split;
+  a.o_f32 = o_dtype == STAR_F32;
+  const dim3 grid((unsigned)((int64_t)d.B * n_query * d.Hq));
+  hipStream_t st = (hipStream_t)stream;
+  if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, dim3(256), 0, st, a);
+  return check_launch();
+}
+
+}  // namespace star

@@ -281,6 +281,58 @@ def decode_loop(q_tail: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# Sampled rows of one kv head (for full-size checks): the same definitions,
+# evaluated for a few rows with one matmul over the query heads sharing K/V.
+# --------------------------------------------------------------------------
+
+def _softmax_rows(S: np.ndarray, V: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row softmax of scores S [h, n] (already scaled, -inf = masked) times V [n, d]."""
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    z = E.sum(axis=1, keepdims=True)
+    return (E @ V) / z, (m + np.log(z))[:, 0]
+
+
+def phase1_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
+                         rows: Sequence[int], block_len: int, anchor_len: int,
+                         scale: float) -> np.ndarray:
+    """Phase-1 outputs of sampled context rows for the query heads of one kv head.
+
+    ``q_rows``: ``[n, h, d]`` queries of rows ``rows[k]`` (h heads sharing this
+    kv head); ``K``, ``V``: ``[L', d]`` context rows of the kv head (at least
+    up to the largest sampled row). Key set as in ``phase1_key_rows``.
+    Returns ``[n, h, d]``.
+    """
+    out = np.zeros(q_rows.shape, dtype=np.float64)
+    for k, r in enumerate(rows):
+        keys = phase1_key_rows(int(r), block_len, anchor_len)
+        Kk = np.asarray(K[keys], dtype=np.float64)
+        Vk = np.asarray(V[keys], dtype=np.float64)
+        S = scale * (np.asarray(q_rows[k], dtype=np.float64) @ Kk.T)
+        out[k], _ = _softmax_rows(S, Vk)
+    return out
+
+
+def phase2_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
+                         positions: Sequence[int], scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense phase-2 outputs and lse of sampled query rows for one kv head.
+
+    ``q_rows``: ``[n, h, d]`` at absolute positions ``positions``; ``K``, ``V``:
+    ``[N, d]`` the whole cache of the kv head (context then tail). Query at
+    position p sees rows ``[0, p]``. Returns ``(O [n, h, d], lse [n, h])``.
+    """
+    n, h, d = q_rows.shape
+    O = np.zeros((n, h, d), dtype=np.float64)
+    LSE = np.zeros((n, h), dtype=np.float64)
+    for k, p in enumerate(positions):
+        Kk = np.asarray(K[:p + 1], dtype=np.float64)
+        Vk = np.asarray(V[:p + 1], dtype=np.float64)
+        S = scale * (np.asarray(q_rows[k], dtype=np.float64) @ Kk.T)
+        O[k], LSE[k] = _softmax_rows(S, Vk)
+    return O, LSE
+
+
+# --------------------------------------------------------------------------
 # Brute force on tiny inputs: scalar loops, math.exp and math.fsum
 # --------------------------------------------------------------------------
 

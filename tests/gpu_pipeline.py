@@ -1,0 +1,116 @@
+"""Runs the hot path through the C ABI on the GPU for a synthetic workload.
+
+Shared by the GPU parity tests, the smoke check and the bench: inputs come
+from the seeded generator, every step is a call of libstarattn through the
+Python binding, torch only allocates device memory.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import long_context_attention_phase1_amd as sa
+from long_context_attention_phase1_amd import synthetic as syn
+
+NAN_BF16 = 0x7FC0
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(x).to(device)
+
+
+def to_host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class Pipeline:
+    """One workload resident on the GPU: inputs, KV cache, outputs."""
+
+    def __init__(self, w: syn.Workload, inputs=None, device="cuda", fill_nan=True, threads=None):
+        self.w = w
+        self.dtype = sa.STAR_BF16 if w.dtype == "bf16" else sa.STAR_F32
+        self.desc = sa.make_desc(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx_len,
+                                 w.block_len, w.anchor_len, w.tail_cap, self.dtype)
+        self.inputs = inputs if inputs is not None else syn.make_inputs(w, threads)
+        self.dev = {k: to_device(v, w.dtype, device) for k, v in self.inputs.items()}
+        self.k_cache = sa.alloc_kv_cache(self.desc, device)
+        self.v_cache = sa.alloc_kv_cache(self.desc, device)
+        if fill_nan:  # unwritten cache rows read as NaN, so a stray read shows up
+            for c in (self.k_cache, self.v_cache):
+                if w.dtype == "bf16":
+                    c.view(torch.int16).fill_(NAN_BF16)
+                else:
+                    c.fill_(float("nan"))
+        elt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.elt = elt
+        self.o_ctx = torch.empty(w.batch, w.ctx_len, w.n_q_heads, w.head_dim, dtype=elt,
+                                 device=device)
+        # per-row tail slices, contiguous
+        self.q_tail_rows = [self.dev["q_tail"][:, t:t + 1].contiguous() for t in range(w.tail_cap)]
+        self.k_tail_rows = [self.dev["k_tail"][:, t:t + 1].contiguous() for t in range(w.tail_cap)]
+        self.v_tail_rows = [self.dev["v_tail"][:, t:t + 1].contiguous() for t in range(w.tail_cap)]
+        self.q_query = self.dev["q_tail"][:, :w.n_query].contiguous()
+        self.k_query = self.dev["k_tail"][:, :w.n_query].contiguous()
+        self.v_query = self.dev["v_tail"][:, :w.n_query].contiguous()
+        self._ws = {}
+
+    # -- phase 1 -----------------------------------------------------------
+    def write_context(self):
+        w = self.w
+        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, 0, self.dev["k_ctx"],
+                         self.dev["v_ctx"], w.ctx_len)
+
+    def phase1(self):
+        sa.star_attn_phase1(self.desc, self.k_cache, self.v_cache, self.dev["q_ctx"], self.o_ctx)
+        return self.o_ctx
+
+    # -- phase 2 -----------------------------------------------------------
+    def workspace(self, kv_len, n_query):
+        n_split = sa.star_attn_phase2_plan(self.desc, kv_len, n_query)
+        key = (n_query, n_split)
+        if key not in self._ws:
+            w = self.w
+            o_part = torch.empty(w.batch, n_query, w.n_q_heads, n_split, w.head_dim,
+                                 dtype=torch.float32, device=self.o_ctx.device)
+            lse_part = torch.empty(w.batch, n_query, w.n_q_heads, n_split, dtype=torch.float32,
+                                   device=self.o_ctx.device)
+            o = torch.empty(w.batch, n_query, w.n_q_heads, w.head_dim, dtype=self.elt,
+                            device=self.o_ctx.device)
+            lse = torch.empty(w.batch, n_query, w.n_q_heads, dtype=torch.float32,
+                              device=self.o_ctx.device)
+            self._ws[key] = (n_split, o_part, lse_part, o, lse)
+        return self._ws[key]
+
+    def attend(self, kv_len, q, n_query):
+        n_split, o_part, lse_part, o, lse = self.workspace(kv_len, n_query)
+        sa.star_attn_phase2_partial(self.desc, self.k_cache, self.v_cache, kv_len, q, n_query,
+                                    o_part, lse_part)
+        sa.star_attn_lse_merge(self.desc, n_query, n_split, o_part, lse_part, o, self.dtype, lse)
+        return o, lse
+
+    def query_step(self):
+        w = self.w
+        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, w.ctx_len, self.k_query,
+                         self.v_query, w.n_query)
+        return self.attend(w.ctx_len + w.n_query, self.q_query, w.n_query)
+
+    def decode_step(self, t):
+        """Decode step t (0-based): append tail row n_query + t, attend with it."""
+        w = self.w
+        row = w.n_query + t
+        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, w.ctx_len + row,
+                         self.k_tail_rows[row], self.v_tail_rows[row], 1)
+        return self.attend(w.ctx_len + row + 1, self.q_tail_rows[row], 1)
+
+    def run_tail(self):
+        """Query step then every decode step; returns host arrays [B, T, Hq, d], [B, T, Hq]."""
+        w = self.w
+        o, lse = self.query_step()
+        outs, lses = [to_host_f64(o)], [lse.cpu().numpy().astype(np.float64)]
+        for t in range(w.n_decode):
+            o, lse = self.decode_step(t)
+            outs.append(to_host_f64(o))
+            lses.append(lse.cpu().numpy().astype(np.float64))
+        return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1)

@@ -303,4 +303,38 @@ def pin_scale_default(orc):
     assert orc.resolve_scale(128, 0.3) == 0.3
 
 
+def pin_sampled_row_forms_match_sdpa(orc):
+    """The per-kv-head sampled-row forms against SDPA (GQA) on every row."""
+    B, L, Hq, Hkv, d = 1, 26, 6, 2, 8
+    q, k, v = _qkv(16, B, L, Hq, Hkv, d)
+    G = Hq // Hkv
+    sc = _scale(orc, d)
+    b, a = 8, 5
+    rows = list(range(L))
+    for g in range(Hkv):
+        o = orc.phase1_rows_one_head(q[0, rows, g * G:(g + 1) * G], k[0, :, g], v[0, :, g],
+                                     rows, b, a, sc)
+        for i in range(-(-L // b)):
+            lo, hi = i * b, min((i + 1) * b, L)
+            if i == 0:
+                ref = _sdpa(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], causal=True)
+            else:
+                cat = lambda x: np.concatenate([x[:, :a], x[:, lo:hi]], axis=1)
+                ref = _sdpa(cat(q), cat(k), cat(v), causal=True)[:, a:]
+            _close(o[lo:hi], ref[0, :, g * G:(g + 1) * G], what=f"sampled phase1 g={g} block {i}")
+    qt, k2, v2, L2, T = _tail_case(17, B=1, Hq=6, Hkv=2)
+    pos = [L2 + j for j in range(T)]
+    ref = _sdpa(qt, k2, v2, mask=_causal_tail_mask(L2, T))
+    tq = torch.from_numpy(qt.transpose(0, 2, 1, 3).copy())
+    tk = torch.from_numpy(k2.transpose(0, 2, 1, 3).copy()).repeat_interleave(3, dim=1)
+    s = torch.matmul(tq, tk.transpose(-1, -2)) * sc
+    s = s.masked_fill(~torch.from_numpy(_causal_tail_mask(L2, T)), -math.inf)
+    lref = torch.logsumexp(s, dim=-1).numpy().transpose(0, 2, 1)
+    for g in range(2):
+        o, l = orc.phase2_rows_one_head(qt[0, :, g * 3:(g + 1) * 3], k2[0, :, g], v2[0, :, g],
+                                        pos, sc)
+        _close(o, ref[0, :, g * 3:(g + 1) * 3], what=f"sampled phase2 g={g}")
+        _close(l, lref[0, :, g * 3:(g + 1) * 3], what=f"sampled phase2 lse g={g}")
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -1,0 +1,197 @@
+"""The C ABI on the CPU: symbols, struct layout, validation and the split plan.
+
+No kernel is launched here: every call either fails validation (which
+happens before anything is enqueued) or is host-only logic.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import long_context_attention_phase1_amd as sa
+from long_context_attention_phase1_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "star_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(star_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sa.load_library()
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_desc_layout_matches_c_compiler():
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "star_attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(star_attn_desc),
+    offsetof(star_attn_desc, batch), offsetof(star_attn_desc, n_q_heads),
+    offsetof(star_attn_desc, n_kv_heads), offsetof(star_attn_desc, head_dim),
+    offsetof(star_attn_desc, ctx_len), offsetof(star_attn_desc, block_len),
+    offsetof(star_attn_desc, anchor_len), offsetof(star_attn_desc, tail_cap),
+    offsetof(star_attn_desc, dtype), offsetof(star_attn_desc, softmax_scale));
+  return 0;
+}'''
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "p.c")
+        exe = os.path.join(td, "p")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c,
+                        "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    D = B.StarAttnDesc
+    want = [ctypes.sizeof(D)] + [getattr(D, f).offset for f, _ in D._fields_]
+    assert got == want
+
+
+def test_abi_version_and_strerror():
+    assert sa.star_attn_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert sa.star_attn_strerror(st) and sa.star_attn_strerror(st) != "unknown status"
+    assert sa.star_attn_strerror(7) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, ctx_len=131072,
+                block_len=16384, anchor_len=16384, tail_cap=320, dtype=B.STAR_BF16,
+                softmax_scale=0.0)
+    base.update(kw)
+    return B.StarAttnDesc(**base)
+
+
+BAD_DESCS = [
+    (dict(batch=0), B.STAR_ERR_INVALID_ARG),
+    (dict(n_q_heads=0), B.STAR_ERR_INVALID_ARG),
+    (dict(ctx_len=0), B.STAR_ERR_INVALID_ARG),
+    (dict(block_len=0), B.STAR_ERR_INVALID_ARG),
+    (dict(anchor_len=0), B.STAR_ERR_INVALID_ARG),
+    (dict(tail_cap=-1), B.STAR_ERR_INVALID_ARG),
+    (dict(softmax_scale=-1.0), B.STAR_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), B.STAR_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), B.STAR_ERR_INVALID_ARG),
+    (dict(dtype=5), B.STAR_ERR_DTYPE),
+    (dict(head_dim=96), B.STAR_ERR_UNSUPPORTED),
+    (dict(n_q_heads=30), B.STAR_ERR_SHAPE),
+    (dict(anchor_len=16385), B.STAR_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DESCS, ids=[str(k) for k, _ in BAD_DESCS])
+def test_bad_desc_rejected_everywhere(kw, code):
+    lib = sa.load_library()
+    d = ctypes.byref(_desc(**kw))
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    n = ctypes.c_int32(-7)
+    assert lib.star_kv_cache_bytes(d) == 0
+    assert lib.star_kv_write(d, fake, fake, 0, fake, fake, 1, None) == code
+    assert lib.star_attn_phase1(d, fake, fake, fake, fake, None) == code
+    assert lib.star_attn_phase2_plan(d, 131073, 1, ctypes.byref(n)) == code
+    assert n.value == -7
+    assert lib.star_attn_phase2_partial(d, fake, fake, 131073, fake, 1, fake, fake, None) == code
+    assert lib.star_attn_lse_merge(d, 1, 4, fake, fake, fake, 0, None, None) == code
+
+
+def test_null_desc_and_pointers():
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(_desc())
+    E = B.STAR_ERR_INVALID_ARG
+    assert lib.star_attn_phase1(None, fake, fake, fake, fake, None) == E
+    assert lib.star_attn_phase1(d, None, fake, fake, fake, None) == E
+    assert lib.star_attn_phase1(d, fake, fake, fake, None, None) == E
+    assert lib.star_kv_write(d, fake, fake, 0, None, fake, 1, None) == E
+    assert lib.star_kv_write(d, fake, fake, 0, fake, fake, 0, None) == E
+    assert lib.star_attn_phase2_partial(d, fake, fake, 131073, fake, 1, None, fake, None) == E
+    assert lib.star_attn_phase2_plan(d, 131073, 1, None) == E
+    assert lib.star_attn_lse_merge(d, 1, 0, fake, fake, fake, 0, None, None) == E
+    assert lib.star_attn_lse_merge(d, 1, 4, fake, fake, fake, 9, None, None) == B.STAR_ERR_DTYPE
+
+
+def test_range_checks():
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(_desc())
+    S = B.STAR_ERR_SHAPE
+    # cache rows [0, L + tail_cap)
+    assert lib.star_kv_write(d, fake, fake, -1, fake, fake, 1, None) == S
+    assert lib.star_kv_write(d, fake, fake, 131072 + 320, fake, fake, 1, None) == S
+    assert lib.star_kv_write(d, fake, fake, 131072 + 300, fake, fake, 21, None) == S
+    # kv_len in [L + 1, L + tail_cap], n_query in [1, kv_len - L]
+    n = ctypes.c_int32()
+    assert lib.star_attn_phase2_plan(d, 131072, 1, ctypes.byref(n)) == S
+    assert lib.star_attn_phase2_plan(d, 131072 + 321, 1, ctypes.byref(n)) == S
+    assert lib.star_attn_phase2_plan(d, 131072 + 5, 6, ctypes.byref(n)) == S
+    assert lib.star_attn_phase2_plan(d, 131072 + 5, 0, ctypes.byref(n)) == B.STAR_ERR_INVALID_ARG
+    assert lib.star_attn_phase2_partial(d, fake, fake, 131072 + 5, fake, 6, fake, fake, None) == S
+    assert lib.star_attn_lse_merge(d, 321, 4, fake, fake, fake, 0, None, None) == S
+
+
+def test_cache_bytes():
+    d = _desc()
+    assert sa.star_kv_cache_bytes(d) == 1 * 8 * (131072 + 320) * 128 * 2
+    d = _desc(ctx_len=100, block_len=40, anchor_len=7, tail_cap=5, dtype=B.STAR_F32,
+              n_q_heads=4, n_kv_heads=2, head_dim=64, batch=3)
+    assert sa.star_kv_cache_bytes(d) == 3 * 2 * 128 * 64 * 4
+
+
+PLAN_CASES = [
+    # (batch, Hq, Hkv, L, blk, anc, tail_cap, kv_len, n_query)
+    (1, 32, 8, 131072, 16384, 16384, 320, 131073, 1),
+    (1, 32, 8, 131072, 16384, 16384, 320, 131072 + 64, 64),
+    (1, 32, 8, 131072, 16384, 16384, 320, 131072 + 320, 1),
+    (1, 32, 8, 1048576, 32768, 32768, 96, 1048576 + 32, 32),
+    (4, 64, 8, 262144, 32768, 32768, 256, 262144 + 128, 128),
+    (4, 64, 8, 262144, 32768, 32768, 256, 262144 + 129, 1),
+    (1, 1, 1, 512, 128, 128, 24, 512 + 16, 16),
+    (2, 4, 4, 333, 100, 37, 7, 333 + 6, 5),
+    (1, 16, 2, 256, 64, 64, 6, 256 + 4, 4),
+    (1, 8, 2, 300, 7, 3, 2000, 300 + 1999, 1999),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES)
+def test_split_plan_covers_cache_once_per_host(case):
+    Bn, Hq, Hkv, L, blk, anc, cap, kv_len, nq = case
+    d = _desc(batch=Bn, n_q_heads=Hq, n_kv_heads=Hkv, ctx_len=L, block_len=blk,
+              anchor_len=anc, tail_cap=cap)
+    n = sa.star_attn_phase2_plan(d, kv_len, nq)
+    assert n >= 1
+    cover = {}
+    last_hi = 0
+    n_blocks = -(-L // blk)
+    for s in range(n):
+        lo, hi, host = sa.star_attn_phase2_split_range(d, kv_len, nq, s)
+        assert 0 <= lo <= hi <= kv_len
+        if lo == hi:
+            continue
+        assert lo == last_hi, "splits must be in order and contiguous"
+        last_hi = hi
+        if host < n_blocks:
+            assert host * blk <= lo and hi <= min((host + 1) * blk, L), (s, lo, hi, host)
+        else:
+            assert host == n_blocks and lo >= L
+        cover[s] = (lo, hi)
+    assert last_hi == kv_len
+    # deterministic
+    assert sa.star_attn_phase2_plan(d, kv_len, nq) == n
+    with pytest.raises(sa.StarAttnError):
+        sa.star_attn_phase2_split_range(d, kv_len, nq, n)

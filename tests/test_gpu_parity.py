@@ -1,0 +1,238 @@
+"""GPU parity: libstarattn (through the C ABI) against the fp64 oracle.
+
+Small workloads checked element by element: several tiles, ragged last
+blocks, block starts not aligned to the 64-row cache tile, anchors shorter
+than the block, GQA 1:1 / 2:1 / 4:1 / 8:1, head_dim 64 and 128, bf16 and
+fp32, the peaked-softmax input, a context shorter than one block, both
+phase-2 kernels (<= 32 and > 32 query columns), empty splits and every
+decode step. Tolerances: max-abs 1e-5 (fp32 workloads) and 2e-2 (bf16
+outputs, fp32 accumulation).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_phase1_amd as sa
+from long_context_attention_phase1_amd import synthetic as syn
+from oracle import star_oracle as orc
+from tests.gpu_pipeline import Pipeline, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+TOL_LSE = {"bf16": 2e-3, "f32": 1e-5}
+
+W = syn.Workload
+CASES = {
+    "tiny_f32": syn.WORKLOADS["tiny_f32"],
+    "gqa4_d128_ragged": W("gqa4_d128_ragged", 1, 8, 2, 128, 640, 256, 256, 8, 3, "bf16", seed=1),
+    "g1_unaligned_a_lt_b": W("g1_unaligned", 2, 4, 4, 128, 333, 100, 37, 5, 2, "bf16", seed=2),
+    "g2_d64_wide_tail": W("g2_d64", 1, 4, 2, 64, 300, 128, 64, 20, 2, "bf16", seed=3),
+    "g8_narrow": W("g8", 1, 16, 2, 128, 256, 64, 64, 4, 2, "bf16", seed=4),
+    "peaked": W("peaked", 1, 4, 1, 128, 512, 128, 128, 3, 2, "bf16", peak_frac=0.05,
+                peak_factor=8.0, seed=5),
+    "one_block": W("one_block", 1, 4, 1, 128, 200, 256, 100, 2, 1, "bf16", seed=6),
+    "f32_gqa_d128": W("f32_gqa", 1, 4, 2, 128, 130, 64, 10, 3, 2, "f32", seed=7),
+    "g4_d64_many_blocks": W("g4_d64", 1, 8, 2, 64, 1024, 128, 128, 40, 1, "bf16", seed=8),
+    # tail longer than one split: early query rows see nothing of the second tail split
+    "long_tail_wide": W("long_tail", 1, 4, 2, 128, 128, 64, 64, 300, 1, "bf16", seed=13),
+    # last block shorter than the split length: its second split is empty
+    "ragged_empty_split": W("ragged_empty", 1, 4, 1, 128, 1100, 512, 300, 2, 2, "bf16", seed=14),
+}
+EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+
+
+def _f64(w, x):
+    return syn.to_f64(x, w.dtype)
+
+
+def _err(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b))))
+
+
+@pytest.fixture(scope="module")
+def runs():
+    _need_gpu()
+    return {}
+
+
+def _pipeline(runs, name):
+    if name not in runs:
+        w = CASES[name]
+        p = Pipeline(w, threads=4)
+        p.write_context()
+        o1 = to_host_f64(p.phase1())
+        tail_o, tail_l = p.run_tail()
+        torch.cuda.synchronize()
+        runs[name] = (p, o1, tail_o, tail_l)
+    return runs[name]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_phase1_matches_oracle(runs, name):
+    p, o1, _, _ = _pipeline(runs, name)
+    w = p.w
+    x = {k: _f64(w, v) for k, v in p.inputs.items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    ref = orc.phase1(x["q_ctx"], x["k_ctx"], x["v_ctx"], w.block_len, w.anchor_len, sc)
+    assert np.isfinite(o1).all()
+    err = _err(o1, ref)
+    print(f"{name}: phase-1 max-abs error {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_phase2_query_and_decode_match_oracle(runs, name):
+    p, _, tail_o, tail_l = _pipeline(runs, name)
+    w = p.w
+    x = {k: _f64(w, v) for k, v in p.inputs.items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    ref_o, ref_l = orc.decode_loop(x["q_tail"], x["k_ctx"], x["v_ctx"], x["k_tail"],
+                                   x["v_tail"], w.n_query, sc)
+    eo, el = _err(tail_o, ref_o), _err(tail_l, ref_l)
+    print(f"{name}: phase-2 max-abs error o {eo:.3e}, lse {el:.3e}")
+    assert eo <= TOL[w.dtype]
+    assert el <= TOL_LSE[w.dtype]
+
+
+@pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g1_unaligned_a_lt_b", "g2_d64_wide_tail",
+                                  "g8_narrow", "f32_gqa_d128", "long_tail_wide",
+                                  "ragged_empty_split"])
+def test_partials_are_the_hosts_replies(runs, name):
+    """Each split's (vector, scalar) equals the oracle's host reply on that range."""
+    p, _, _, _ = _pipeline(runs, name)
+    w = p.w
+    x = {k: _f64(w, v) for k, v in p.inputs.items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    kv_len = w.ctx_len + w.n_query
+    n_split, o_part, lse_part, _, _ = p.workspace(kv_len, w.n_query)
+    sa.star_attn_phase2_partial(p.desc, p.k_cache, p.v_cache, kv_len, p.q_query, w.n_query,
+                                o_part, lse_part)
+    torch.cuda.synchronize()
+    op, lp = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    k_all = np.concatenate([x["k_ctx"], x["k_tail"][:, :w.n_query]], axis=1)
+    v_all = np.concatenate([x["v_ctx"], x["v_tail"][:, :w.n_query]], axis=1)
+    G = w.group
+    n_empty = 0
+    for sg in range(n_split):
+        lo, hi, host = sa.star_attn_phase2_split_range(p.desc, kv_len, w.n_query, sg)
+        for s in range(w.batch):
+            for j in range(w.n_query):
+                for h in range(w.n_q_heads):
+                    ro, rl = orc.phase2_partial(x["q_tail"][s, j, h], k_all[s, :, h // G],
+                                                v_all[s, :, h // G], w.ctx_len + j, lo, hi, sc)
+                    if rl == -np.inf:
+                        n_empty += 1
+                        assert lp[s, j, h, sg] == -np.inf and np.all(op[s, j, h, sg] == 0.0)
+                        continue
+                    tol = 1e-5 if w.dtype == "f32" else 1e-2
+                    assert _err(op[s, j, h, sg], ro) <= tol, (sg, s, j, h)
+                    assert abs(lp[s, j, h, sg] - rl) <= TOL_LSE[w.dtype]
+    if name in EMPTY_SPLIT_CASES:
+        assert n_empty > 0
+
+
+def test_golden_fixture_on_gpu():
+    _need_gpu()
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_ragged_bf16.json")
+    doc = json.load(open(path))
+    w = W(**doc["workload"])
+    p = Pipeline(w, threads=1)
+    p.write_context()
+    o1 = to_host_f64(p.phase1()).ravel()
+    o2, l2 = p.query_step()
+    torch.cuda.synchronize()
+    assert _err(o1, doc["phase1_out"]) <= TOL["bf16"]
+    assert _err(to_host_f64(o2).ravel(), doc["phase2_out"]) <= TOL["bf16"]
+    assert _err(l2.cpu().numpy().ravel(), doc["phase2_lse"]) <= TOL_LSE["bf16"]
+
+
+def test_kv_write_layout_bit_exact():
+    _need_gpu()
+    for dtype, d in (("bf16", 128), ("bf16", 64), ("f32", 64)):
+        w = W("layout", 2, 6, 3, d, 150, 64, 64, 9, 0, dtype, seed=9)
+        p = Pipeline(w, threads=1)
+        p.write_context()
+        # tail rows in two unaligned pieces
+        sa.star_kv_write(p.desc, p.k_cache, p.v_cache, w.ctx_len, p.k_query[:, :4].contiguous(),
+                         p.v_query[:, :4].contiguous(), 4)
+        sa.star_kv_write(p.desc, p.k_cache, p.v_cache, w.ctx_len + 5,
+                         p.k_query[:, 5:9].contiguous(), p.v_query[:, 5:9].contiguous(), 4)
+        torch.cuda.synchronize()
+        R = -(-(w.ctx_len + w.tail_cap) // 64) * 64
+        raw = np.uint16 if dtype == "bf16" else np.uint32
+        kc = p.k_cache.view(torch.int16 if dtype == "bf16" else torch.int32).cpu().numpy().view(raw)
+        vc = p.v_cache.view(torch.int16 if dtype == "bf16" else torch.int32).cpu().numpy().view(raw)
+        kc = kc.reshape(w.batch, w.n_kv_heads, R, d)
+        vc = vc.reshape(w.batch, w.n_kv_heads, R // 64, d, 64)
+        k_rows = np.concatenate([p.inputs["k_ctx"], p.inputs["k_tail"][:, :9]], axis=1).view(raw)
+        v_rows = np.concatenate([p.inputs["v_ctx"], p.inputs["v_tail"][:, :9]], axis=1).view(raw)
+        nan = 0x7FC0 if dtype == "bf16" else np.float32(np.nan).view(np.uint32)
+        for r in range(R):
+            written = r < w.ctx_len + 4 or (w.ctx_len + 5 <= r < w.ctx_len + 9)
+            for s in range(w.batch):
+                for g in range(w.n_kv_heads):
+                    kr = kc[s, g, r]
+                    vr = vc[s, g, r // 64, :, r % 64]
+                    if written:
+                        assert np.array_equal(kr, k_rows[s, r, g]), (dtype, d, r, s, g)
+                        assert np.array_equal(vr, v_rows[s, r, g]), (dtype, d, r, s, g)
+                    else:
+                        assert np.all(kr == nan) and np.all(vr == nan), (dtype, d, r)
+
+
+def test_phase1_is_deterministic_and_blocks_independent():
+    _need_gpu()
+    w = W("indep", 1, 8, 2, 128, 768, 256, 256, 1, 0, "bf16", seed=10)
+    p = Pipeline(w, threads=1)
+    p.write_context()
+    a = p.phase1().clone()
+    b = p.phase1().clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # perturb block 1 (rows 256..511): blocks 0 and 2 must not change at all
+    p.dev["q_ctx"][:, 256:512] *= -1
+    k2 = p.dev["k_ctx"].clone()
+    v2 = p.dev["v_ctx"].clone()
+    k2[:, 256:512] += 1.0
+    v2[:, 256:512] -= 0.5
+    sa.star_kv_write(p.desc, p.k_cache, p.v_cache, 0, k2, v2, w.ctx_len)
+    c = p.phase1().clone()
+    torch.cuda.synchronize()
+    ai, ci = a.view(torch.int16), c.view(torch.int16)
+    assert torch.equal(ai[:, :256], ci[:, :256])
+    assert torch.equal(ai[:, 512:], ci[:, 512:])
+    assert not torch.equal(ai[:, 256:512], ci[:, 256:512])
+
+
+def test_phase2_is_deterministic():
+    _need_gpu()
+    w = CASES["gqa4_d128_ragged"]
+    p = Pipeline(w, threads=1)
+    p.write_context()
+    o1, l1 = p.query_step()
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = p.query_step()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_binding_rejects_wrong_buffers():
+    _need_gpu()
+    w = CASES["g8_narrow"]
+    p = Pipeline(w, threads=1)
+    bad = torch.empty(1, 3, dtype=p.elt, device="cuda")
+    with pytest.raises(ValueError):
+        sa.star_attn_phase1(p.desc, p.k_cache, p.v_cache, bad, p.o_ctx)
+    with pytest.raises(ValueError):
+        sa.star_attn_phase1(p.desc, p.k_cache[:10], p.v_cache, p.dev["q_ctx"], p.o_ctx)
+    with pytest.raises(sa.StarAttnError):
+        sa.star_attn_phase2_plan(p.desc, w.ctx_len, 1)

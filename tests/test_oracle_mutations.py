@@ -96,6 +96,18 @@ MUTANTS = [
     ("decode_query_step_sees_all_tail",
      "[L + j for j in range(n_query)], scale)",
      "[L + n_query - 1 for j in range(n_query)], scale)"),
+    ("sampled_p1_no_anchor",
+     "keys = phase1_key_rows(int(r), block_len, anchor_len)",
+     "keys = phase1_key_rows(int(r), block_len, 0)[anchor_len * 0:] if r < block_len else np.arange(r // block_len * block_len, r + 1)"),
+    ("sampled_p2_excludes_self",
+     "Kk = np.asarray(K[:p + 1], dtype=np.float64)\n        Vk = np.asarray(V[:p + 1], dtype=np.float64)",
+     "Kk = np.asarray(K[:p], dtype=np.float64)\n        Vk = np.asarray(V[:p], dtype=np.float64)"),
+    ("sampled_softmax_lse_log2",
+     "return (E @ V) / z, (m + np.log(z))[:, 0]",
+     "return (E @ V) / z, (m + np.log2(z))[:, 0]"),
+    ("sampled_softmax_unnormalised",
+     "return (E @ V) / z, (m + np.log(z))[:, 0]",
+     "return (E @ V), (m + np.log(z))[:, 0]"),
 ]
 
 
