@@ -261,12 +261,168 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[NKT], float& m, float
     }
 }
 
+// ---- wide kernel, interior tiles: 4-stage direct-to-LDS pipeline -------------
+//
+// Interior tiles (all 64 keys visible to every query column of the
+// workgroup) are loaded with global_load_lds_dwordx4, which writes lane i's
+// 16 bytes at LDS base + 16*i: each lane fetches the global chunk that the
+// swizzled LDS layout wants at its slot. Tiles are prefetched two ahead into
+// a ring of four stages. The loop is software-pipelined: while the softmax
+// of tile t runs on the VALU, the MFMAs of S(t+1) = K(t+1) Q^T are issued.
+//
+// Lazy rescale: the running max m of a column only moves when a tile's max
+// exceeds it by more than kTau in the exp2 domain, so P <= 2^kTau and the O
+// accumulators are rescaled (by exp2((m_old - m_new) * c2)) only on those
+// tiles; the final O / l uses the same m, so the result is unchanged.
+constexpr float kTau = 8.0f;
+constexpr int kStages = 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+struct Geo {
+  static constexpr int CH = D / 8;              // 16-byte chunks per K row
+  static constexpr int RB = 2 * D;              // bytes per K row
+  static constexpr int KBYTES = 64 * RB;        // K tile
+  static constexpr int VBYTES = D * 128;        // transposed V tile (D rows x 64 keys)
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KI = KBYTES / 1024 / 4;  // 1-KB DMA instructions per wave, K
+  static constexpr int VI = VBYTES / 1024 / 4;  // and V
+  static constexpr int PER = KI + VI;           // DMA instructions per thread per tile
+  static constexpr int SPK = 1024 / RB;         // K slots per KB
+  static constexpr int KS = D / 16;             // k-steps over the head dimension
+  static constexpr int DT = D / 32;             // 32-row tiles of the output dimension
+};
+
+// s_waitcnt vmcnt(N) leaving expcnt / lgkmcnt untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile(char* stage, const uint16_t* K, const uint16_t* V,
+                                         int64_t kbase, int w, int lane) {
+  using Gm = Geo<D>;
+#pragma unroll
+  for (int j = 0; j < Gm::KI; ++j) {
+    const int kb = Gm::KI * w + j;
+    const int slot = Gm::SPK * kb + lane / Gm::CH;
+    const int c = (lane % Gm::CH) ^ (slot & (Gm::CH - 1));
+    const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
+    __builtin_amdgcn_global_load_lds((const void*)(K + key * D + 8 * c),
+                                     (lds_void*)(stage + kb * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < Gm::VI; ++j) {
+    const int kb = Gm::VI * w + j;
+    const int e = 8 * kb + (lane >> 3);
+    const int kc = (lane & 7) ^ (e & 7);
+    __builtin_amdgcn_global_load_lds((const void*)(V + kbase * D + e * 64 + 8 * kc),
+                                     (lds_void*)(stage + Gm::KBYTES + kb * 1024), 16, 0, 0);
+  }
+}
+
+// S^T for the 64 keys of a stage: s[qt][kt] (kt: 32-key slice).
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* st, const u32x4 (&q)[2][Geo<D>::KS],
+                                        f32x16 (&s)[2][2], int l32, int g) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < Geo<D>::KS; ++ks) {
+      const u32x4 kop = lds16(st + k_off<D>(32 * kt + l32, 2 * ks + g));
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        s[qt][kt] = mfma_bf16(kop, q[qt][ks], ks == 0 ? f32x16{} : s[qt][kt]);
+    }
+}
+
+// O^T += V^T P^T for the 64 keys of a stage.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* st, const u32x4 (&p)[2][2][2],
+                                        f32x16 (&o)[2][Geo<D>::DT], int l32, int g) {
+#pragma unroll
+  for (int dt = 0; dt < Geo<D>::DT; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 vop =
+            lds16(st + Geo<D>::KBYTES + v_off(32 * dt + l32, 4 * kt + 2 * kb + g));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma_bf16(vop, p[qt][kt][kb], o[qt][dt]);
+      }
+}
+
+// max / sum with the lane 32 apart (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lazy-rescale online softmax of the two column tiles; returns the
+// wave-uniform "rescale O" flag, the per-column factors and the bf16 P.
+__device__ __forceinline__ bool softmax_lazy(f32x16 (&s)[2][2], float (&m)[2], float (&l)[2],
+                                             float (&alpha)[2], u32x4 (&p)[2][2][2], float c2) {
+  float mx[2];
+  bool need = false;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float x = fmaxf(s[qt][0][0], s[qt][1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(s[qt][0][i], s[qt][1][i]));
+    x = pair_max(x);
+    mx[qt] = x;
+    need |= (x - m[qt]) * c2 > kTau;
+  }
+  const bool any = __any(need);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float m_new = any ? fmaxf(m[qt], mx[qt]) : m[qt];
+    alpha[qt] = fast_exp2((m[qt] - m_new) * c2);
+    m[qt] = m_new;
+    const float mc = m_new * c2;
+    float rs = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(fmaf(s[qt][kt][i], c2, -mc));
+        s[qt][kt][i] = e;
+        rs += e;
+      }
+    l[qt] = l[qt] * alpha[qt] + rs;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int b = kb * 8;
+        const f32x16& x = s[qt][kt];
+        p[qt][kt][kb] = u32x4{pack_bf16(x[b + 0], x[b + 1]), pack_bf16(x[b + 2], x[b + 3]),
+                              pack_bf16(x[b + 4], x[b + 5]), pack_bf16(x[b + 6], x[b + 7])};
+      }
+  }
+  return any;
+}
+
 template <int D, bool PHASE1>
 __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
-  constexpr int KS = D / 16;  // k-steps over the head dimension
-  constexpr int DT = D / 32;  // 32-row tiles of the output dimension
+  using Gm = Geo<D>;
+  constexpr int KS = Gm::KS, DT = Gm::DT;
   using Tile = WideTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Tile::STAGE];
+  static_assert(Tile::STAGE == Gm::STAGE, "stage geometry");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * Gm::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -279,7 +435,7 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
   const int hw = w % a.HW, rw = w / a.HW;
   const int head = kvh * a.G + hq * a.HW + hw;
 
-  int64_t row0, row_end, loA = 0, hiA = 0, loB, hiB, pos_off;
+  int64_t row0, row_end, hiA = 0, loB, hiB, pos_off;
   int32_t sigma = 0;
   if (PHASE1) {
     // heaviest tiles first: anchored blocks by descending row tile, then block 0
@@ -314,6 +470,7 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
   const uint16_t* K = a.k + head_row0 * D;
   const uint16_t* V = a.v + head_row0 * D;
+  const float c2 = a.c2;
 
   // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g
   u32x4 qop[2][KS];
@@ -334,81 +491,106 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x16{};
   float m[2] = {kMinit, kMinit}, l[2] = {0.0f, 0.0f};
 
-  const int nA = hiA > loA ? (int)cdiv64(hiA, 64) : 0;
-  const int64_t kb0 = (loB / 64) * 64;
-  const int nB = hiB > loB ? (int)cdiv64(hiB - kb0, 64) : 0;
-  const int nT = nA + nB;
+  // ---- tile classes. Range A: anchor [0, hiA), no mask. Range B: [loB, hiB),
+  // causal (key <= query position). Interior tiles need no mask at all.
   const int64_t min_pos = row0 + pos_off;
+  const int nAi = (int)(hiA / 64);
+  const bool a_edge = (hiA % 64) != 0;
+  int64_t bf = 0, bl = 0, i0 = 0, i1 = 0;
+  if (hiB > loB) {
+    bf = loB / 64;
+    bl = cdiv64(hiB, 64);
+    int64_t t1 = hiB / 64;
+    const int64_t tp = (min_pos + 1) / 64;
+    if (tp < t1) t1 = tp;
+    const int64_t t0 = cdiv64(loB, 64);
+    i0 = t0 > bf ? t0 : bf;
+    i1 = t1 < bl ? t1 : bl;
+    if (i1 < i0) i1 = i0;
+  }
+  const int n_int = nAi + (int)(i1 - i0);
+  auto int_kbase = [&](int j) -> int64_t {
+    j = j < n_int ? j : n_int - 1;
+    return j < nAi ? (int64_t)j * 64 : (i0 + (j - nAi)) * 64;
+  };
 
-  if (nT > 0) {
-    Tile st;
-    {
-      const bool inA = 0 < nA;
-      st.load(K, V, inA ? 0 : kb0, inA ? loA : loB, inA ? hiA : hiB, tid);
-      st.store(smem, tid);
-    }
-    __syncthreads();
-    for (int t = 0; t < nT; ++t) {
-      if (t + 1 < nT) {
-        const bool inA = t + 1 < nA;
-        st.load(K, V, inA ? (int64_t)(t + 1) * 64 : kb0 + (int64_t)(t + 1 - nA) * 64,
-                inA ? loA : loB, inA ? hiA : hiB, tid);
+  if (n_int > 0) {
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j) dma_tile<D>(smem + j * Gm::STAGE, K, V, int_kbase(j), w, lane);
+    wait_vmcnt<2 * Gm::PER>();
+    __builtin_amdgcn_s_barrier();
+    f32x16 sc[2][2];
+    qk_tile<D>(smem, qop, sc, l32, g);
+    for (int t = 0; t < n_int; ++t) {
+      wait_vmcnt<Gm::PER>();
+      __builtin_amdgcn_s_barrier();
+      dma_tile<D>(smem + ((t + 3) & 3) * Gm::STAGE, K, V, int_kbase(t + 3), w, lane);
+      f32x16 sn[2][2];
+      qk_tile<D>(smem + ((t + 1) & 3) * Gm::STAGE, qop, sn, l32, g);
+      float alpha[2];
+      u32x4 p[2][2][2];
+      if (softmax_lazy(sc, m, l, alpha, p, c2)) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha[qt];
       }
-      const char* buf = smem + (t & 1) * Tile::STAGE;
-      const bool inA = t < nA;
-      const int64_t kbase = inA ? (int64_t)t * 64 : kb0 + (int64_t)(t - nA) * 64;
-      const int64_t lo = inA ? loA : loB, hi = inA ? hiA : hiB;
-      const bool causal = !inA;
-      const bool edge = kbase < lo || kbase + 64 > hi || (causal && kbase + 63 > min_pos);
-
-      f32x16 sacc[2][2];
+      pv_tile<D>(smem + (t & 3) * Gm::STAGE, p, oacc, l32, g);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc[qt][kt] = f32x16{};
+        for (int kt = 0; kt < 2; ++kt) sc[qt][kt] = sn[qt][kt];
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // ---- edge tiles: masked, synchronous, staged through registers with zero fill
+  const int n_edge = (a_edge ? 1 : 0) + (int)(i0 - bf) + (int)(bl - i1);
+  for (int e = 0; e < n_edge; ++e) {
+    int64_t kbase, lo, hi;
+    bool causal;
+    int k = e;
+    if (a_edge && k == 0) {
+      kbase = (int64_t)nAi * 64; lo = 0; hi = hiA; causal = false;
+    } else {
+      k -= a_edge ? 1 : 0;
+      kbase = (k < i0 - bf ? bf + k : i1 + (k - (i0 - bf))) * 64;
+      lo = loB; hi = hiB; causal = true;
+    }
+    Tile st;
+    st.load(K, V, kbase, lo, hi, tid);
+    st.store(smem, tid);
+    block_sync_lds();
+    f32x16 sc[2][2];
+    qk_tile<D>(smem, qop, sc, l32, g);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int64_t pos = wrow0 + 32 * qt + l32 + pos_off;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kop = lds16(buf + k_off<D>(32 * kt + l32, 2 * ks + g));
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) sacc[qt][kt] = mfma_bf16(kop, qop[qt][ks], sacc[qt][kt]);
+        for (int i = 0; i < 16; ++i) {
+          const int64_t key = kbase + 32 * kt + acc_key(i, g);
+          if (key < lo || key >= hi || (causal && key > pos)) sc[qt][kt][i] = -INFINITY;
         }
-      if (edge) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const int64_t pos = wrow0 + 32 * qt + l32 + pos_off;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int64_t key = kbase + 32 * kt + acc_key(i, g);
-              if (key < lo || key >= hi || (causal && key > pos)) sacc[qt][kt][i] = -INFINITY;
-            }
-        }
-      }
-      u32x4 p[2][2][2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) softmax_update<2, DT>(sacc[qt], m[qt], l[qt], oacc[qt], p[qt], a.c2);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const u32x4 vop = lds16(buf + Tile::KBYTES + v_off(32 * dt + l32, 4 * kt + 2 * kb + g));
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) oacc[qt][dt] = mfma_bf16(vop, p[qt][kt][kb], oacc[qt][dt]);
-          }
-      if (t + 1 < nT) st.store(smem + ((t + 1) & 1) * Tile::STAGE, tid);
-      __syncthreads();
     }
+    float alpha[2];
+    u32x4 p[2][2][2];
+    if (softmax_lazy(sc, m, l, alpha, p, c2)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha[qt];
+    }
+    pv_tile<D>(smem, p, oacc, l32, g);
+    block_sync_lds();
   }
 
   // ---- epilogue: accumulator element i of tile dt is dimension 32*dt + 8*(i/4) + 4*g + i%4
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+    const float lt = pair_sum(l[qt]);
     const int64_t r = wrow0 + 32 * qt + l32;
     if (r >= row_end) continue;
     if (PHASE1) {
