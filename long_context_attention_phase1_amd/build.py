@@ -18,8 +18,11 @@ ARCH = "gfx950"
 
 SOURCES = ["star_host.cpp", "star_kernels.hip"]
 
-# Packed fp32 ALU ops are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Device code: no packed fp32 ALU ops; IEEE mode off and no NaN operands
+# (lets max chains fold into v_max3_f32 without canonicalizing every MFMA
+# result). Host code keeps full IEEE semantics (its argument checks test NaN).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-Xarch_device", "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans"]
 
 
 def command(out: str = LIB, extra=()) -> list:

@@ -80,8 +80,11 @@ __device__ __forceinline__ uint32_t k_off(int slot, int c) {
   return (uint32_t)(slot * (D * 2) + ((c ^ (slot & (D / 8 - 1))) << 4));
 }
 // LDS byte offset of key chunk kc (8 keys) of row e of a transposed V tile.
+// The XOR with bits 1..3 of e spreads the 16 lanes of one LDS cycle (rows
+// e .. e+15, same kc) over all 64 banks.
+__device__ __forceinline__ int v_swz(int e) { return (e >> 1) & 7; }
 __device__ __forceinline__ uint32_t v_off(int e, int kc) {
-  return (uint32_t)(e * 128 + ((kc ^ (e & 7)) << 4));
+  return (uint32_t)(e * 128 + ((kc ^ v_swz(e)) << 4));
 }
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *(const u32x4*)p; }
@@ -168,7 +171,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel: 4 waves x 64 query columns share 64-key K / V^T tiles in LDS.
+// Wide kernel: NW waves x (32 * QT) query columns share 64-key K / V^T tiles
+// in LDS. Columns are (query row, head) pairs of one kv head.
 // ---------------------------------------------------------------------------
 struct WideArgs {
   const uint16_t* k;  // cache K (row-major rows)
@@ -185,43 +189,6 @@ struct WideArgs {
   int32_t Hq, Hkv, G, HW, HQ, NG, NRT;  // NRT: row tiles (phase 1) / query tiles (phase 2)
   int32_t BM;                           // rows per workgroup = 64 * (4 / HW)
   float scale, c2;                      // softmax scale and scale*log2(e)
-};
-
-template <int D>
-struct WideTile {
-  static constexpr int CH = D / 8;          // 16-byte chunks per K row
-  static constexpr int KPT = 64 * CH / 256; // K chunks per thread
-  static constexpr int VPT = D * 8 / 256;   // V chunks per thread
-  static constexpr int KBYTES = 64 * D * 2;
-  static constexpr int STAGE = 2 * KBYTES;  // K tile + V^T tile
-  u32x4 kr[KPT], vr[VPT];
-
-  __device__ __forceinline__ void load(const uint16_t* K, const uint16_t* V, int64_t kbase,
-                                       int64_t lo, int64_t hi, int tid) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 256 * i, slot = u / CH, c = u % CH;
-      const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
-      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + 256 * i, e = u >> 3, kc = u & 7;
-      vr[i] = load_v_chunk(V + kbase * D + e * 64 + kc * 8, kbase + kc * 8, lo, hi);
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 256 * i;
-      sts16(lds + k_off<D>(u / CH, u % CH), kr[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + 256 * i;
-      sts16(lds + KBYTES + v_off(u >> 3, u & 7), vr[i]);
-    }
-  }
 };
 
 // Online-softmax update of one query-column tile from raw scores s[kt]
@@ -261,37 +228,54 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[NKT], float& m, float
     }
 }
 
-// ---- wide kernel, interior tiles: 4-stage direct-to-LDS pipeline -------------
+// max / sum with the lane 32 apart (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- geometry ----------------------------------------------------------------
 //
 // Interior tiles (all 64 keys visible to every query column of the
 // workgroup) are loaded with global_load_lds_dwordx4, which writes lane i's
 // 16 bytes at LDS base + 16*i: each lane fetches the global chunk that the
 // swizzled LDS layout wants at its slot. Tiles are prefetched two ahead into
-// a ring of four stages. The loop is software-pipelined: while the softmax
-// of tile t runs on the VALU, the MFMAs of S(t+1) = K(t+1) Q^T are issued.
+// a ring of four stages; the LDS holds the four K tiles, then the four
+// transposed V tiles, so every operand read is a per-lane register plus an
+// immediate below 64 KB. The loop is software-pipelined per 32-key slice:
+// while the softmax of slice u runs on the VALU, the MFMAs of S(u+1) are
+// issued, and the row max of S(u+1) overlaps the P.V MFMAs of slice u.
 //
-// Lazy rescale: the running max m of a column only moves when a tile's max
+// Lazy rescale: the running max m of a column only moves when a slice max
 // exceeds it by more than kTau in the exp2 domain, so P <= 2^kTau and the O
-// accumulators are rescaled (by exp2((m_old - m_new) * c2)) only on those
-// tiles; the final O / l uses the same m, so the result is unchanged.
+// accumulators are rescaled (by exp2((m_old - m_new) * c2)) only then; the
+// final O / l uses the same m, so the result is unchanged.
 constexpr float kTau = 8.0f;
 constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D>
+template <int D, int NW>
 struct Geo {
+  static constexpr int NT = 64 * NW;             // threads
   static constexpr int CH = D / 8;              // 16-byte chunks per K row
   static constexpr int RB = 2 * D;              // bytes per K row
   static constexpr int KBYTES = 64 * RB;        // K tile
   static constexpr int VBYTES = D * 128;        // transposed V tile (D rows x 64 keys)
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KI = KBYTES / 1024 / 4;  // 1-KB DMA instructions per wave, K
-  static constexpr int VI = VBYTES / 1024 / 4;  // and V
+  static constexpr int K_AT = 0;                // ring: K tiles of the stages
+  static constexpr int V_AT = kStages * KBYTES; //       then V tiles
+  static constexpr int RING = kStages * (KBYTES + VBYTES);
+  static constexpr int KI = KBYTES / 1024 / NW; // 1-KB DMA instructions per wave, K
+  static constexpr int VI = VBYTES / 1024 / NW; // and V
   static constexpr int PER = KI + VI;           // DMA instructions per thread per tile
   static constexpr int SPK = 1024 / RB;         // K slots per KB
   static constexpr int KS = D / 16;             // k-steps over the head dimension
   static constexpr int DT = D / 32;             // 32-row tiles of the output dimension
+  static_assert(KI >= 1 && VI >= 1, "tile too small for the wave count");
 };
 
 // s_waitcnt vmcnt(N) leaving expcnt / lgkmcnt untouched (gfx9 encoding).
@@ -306,123 +290,225 @@ __device__ __forceinline__ void block_sync_lds() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int D>
-__device__ __forceinline__ void dma_tile(char* stage, const uint16_t* K, const uint16_t* V,
-                                         int64_t kbase, int w, int lane) {
-  using Gm = Geo<D>;
+// Register-staged tile load for edge tiles: zero for keys outside [lo, hi),
+// written into stage 0 of the ring.
+template <int D, int NW>
+struct EdgeTile {
+  using Gm = Geo<D, NW>;
+  static constexpr int KPT = 64 * Gm::CH / Gm::NT;
+  static constexpr int VPT = D * 8 / Gm::NT;
+  u32x4 kr[KPT], vr[VPT];
+
+  __device__ __forceinline__ void load(const uint16_t* K, const uint16_t* V, int64_t kbase,
+                                       int64_t lo, int64_t hi, int tid) {
 #pragma unroll
-  for (int j = 0; j < Gm::KI; ++j) {
-    const int kb = Gm::KI * w + j;
-    const int slot = Gm::SPK * kb + lane / Gm::CH;
-    const int c = (lane % Gm::CH) ^ (slot & (Gm::CH - 1));
-    const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
-    __builtin_amdgcn_global_load_lds((const void*)(K + key * D + 8 * c),
-                                     (lds_void*)(stage + kb * 1024), 16, 0, 0);
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + Gm::NT * i, slot = u / Gm::CH, c = u % Gm::CH;
+      const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
+      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + Gm::NT * i, e = u >> 3, kc = u & 7;
+      vr[i] = load_v_chunk(V + kbase * D + e * 64 + kc * 8, kbase + kc * 8, lo, hi);
+    }
   }
+  __device__ __forceinline__ void store(char* smem, int tid) const {
 #pragma unroll
-  for (int j = 0; j < Gm::VI; ++j) {
-    const int kb = Gm::VI * w + j;
-    const int e = 8 * kb + (lane >> 3);
-    const int kc = (lane & 7) ^ (e & 7);
-    __builtin_amdgcn_global_load_lds((const void*)(V + kbase * D + e * 64 + 8 * kc),
-                                     (lds_void*)(stage + Gm::KBYTES + kb * 1024), 16, 0, 0);
+    for (int i = 0; i < KPT; ++i) {
+      const int u = tid + Gm::NT * i;
+      sts16(smem + Gm::K_AT + k_off<D>(u / Gm::CH, u % Gm::CH), kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + Gm::NT * i;
+      sts16(smem + Gm::V_AT + v_off(u >> 3, u & 7), vr[i]);
+    }
+  }
+};
+
+// Per-lane constant offsets, computed once per workgroup.
+template <int D, int NW>
+struct LaneOffsets {
+  using Gm = Geo<D, NW>;
+  uint32_t kq[Gm::KS];  // K operand, slice 0, k-step ks (bytes inside a K tile)
+  uint32_t vq[2][2];    // V operand, [kt][kb], dt = 0 (bytes from the ring start)
+  uint32_t kd[Gm::KI];  // DMA: global byte offset of this lane's K chunk in a tile
+  uint32_t vd[Gm::VI];  // DMA: global byte offset of this lane's V chunk in a tile
+
+  __device__ __forceinline__ void init(int l32, int g, int w, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks) kq[ks] = k_off<D>(l32, 2 * ks + g);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        vq[kt][kb] = (uint32_t)Gm::V_AT + v_off(l32, 4 * kt + 2 * kb + g);
+#pragma unroll
+    for (int j = 0; j < Gm::KI; ++j) {
+      const int slot = Gm::SPK * (Gm::KI * w + j) + lane / Gm::CH;
+      const int c = (lane % Gm::CH) ^ (slot & (Gm::CH - 1));
+      kd[j] = (uint32_t)(((slot & 32) + swap23(slot & 31)) * Gm::RB + 16 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < Gm::VI; ++j) {
+      const int e = 8 * (Gm::VI * w + j) + (lane >> 3);
+      const int kc = (lane & 7) ^ v_swz(e);
+      vd[j] = (uint32_t)((e * 64 + 8 * kc) * 2);
+    }
+  }
+};
+
+template <int D, int NW, int ST>
+__device__ __forceinline__ void dma_stage(char* smem, const char* Kt, const char* Vt,
+                                          const LaneOffsets<D, NW>& lo, int w) {
+  using Gm = Geo<D, NW>;
+#pragma unroll
+  for (int j = 0; j < Gm::KI; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)(Kt + lo.kd[j]),
+                                     (lds_void*)(smem + Gm::K_AT + ST * Gm::KBYTES +
+                                                 (Gm::KI * w + j) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < Gm::VI; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)(Vt + lo.vd[j]),
+                                     (lds_void*)(smem + Gm::V_AT + ST * Gm::VBYTES +
+                                                 (Gm::VI * w + j) * 1024), 16, 0, 0);
+}
+
+// S^T of one 32-key slice KT of stage ST for the QT column tiles.
+template <int D, int NW, int QT, int ST, int KT>
+__device__ __forceinline__ void qk_slice(const char* smem, const LaneOffsets<D, NW>& lo,
+                                         const u32x4 (&q)[QT][Geo<D, NW>::KS], f32x16 (&s)[QT]) {
+  using Gm = Geo<D, NW>;
+#pragma unroll
+  for (int ks = 0; ks < Gm::KS; ++ks) {
+    const u32x4 kop = lds16(smem + lo.kq[ks] + (Gm::K_AT + ST * Gm::KBYTES + KT * 32 * Gm::RB));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) s[qt] = mfma_bf16(kop, q[qt][ks], ks == 0 ? f32x16{} : s[qt]);
   }
 }
 
-// S^T for the 64 keys of a stage: s[qt][kt] (kt: 32-key slice).
-template <int D>
-__device__ __forceinline__ void qk_tile(const char* st, const u32x4 (&q)[2][Geo<D>::KS],
-                                        f32x16 (&s)[2][2], int l32, int g) {
+// O^T += V^T P^T for one 32-key slice KT of stage ST.
+template <int D, int NW, int QT, int ST, int KT>
+__device__ __forceinline__ void pv_slice(const char* smem, const LaneOffsets<D, NW>& lo,
+                                         const u32x4 (&p)[QT][2], f32x16 (&o)[QT][Geo<D, NW>::DT]) {
+  using Gm = Geo<D, NW>;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < Geo<D>::KS; ++ks) {
-      const u32x4 kop = lds16(st + k_off<D>(32 * kt + l32, 2 * ks + g));
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4 vop = lds16(smem + lo.vq[KT][kb] + (ST * Gm::VBYTES + dt * 32 * 128));
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        s[qt][kt] = mfma_bf16(kop, q[qt][ks], ks == 0 ? f32x16{} : s[qt][kt]);
+      for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mfma_bf16(vop, p[qt][kb], o[qt][dt]);
     }
 }
 
-// O^T += V^T P^T for the 64 keys of a stage.
-template <int D>
-__device__ __forceinline__ void pv_tile(const char* st, const u32x4 (&p)[2][2][2],
-                                        f32x16 (&o)[2][Geo<D>::DT], int l32, int g) {
+template <int QT>
+__device__ __forceinline__ void slice_max3(const f32x16 (&s)[QT], float (&mx)[QT]) {
 #pragma unroll
-  for (int dt = 0; dt < Geo<D>::DT; ++dt)
+  for (int qt = 0; qt < QT; ++qt) {
+    float x = fmaxf(s[qt][0], fmaxf(s[qt][1], s[qt][2]));
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 vop =
-            lds16(st + Geo<D>::KBYTES + v_off(32 * dt + l32, 4 * kt + 2 * kb + g));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma_bf16(vop, p[qt][kt][kb], o[qt][dt]);
-      }
+    for (int i = 3; i < 15; i += 2) x = fmaxf(x, fmaxf(s[qt][i], s[qt][i + 1]));
+    x = fmaxf(x, s[qt][15]);
+    mx[qt] = pair_max(x);
+  }
 }
 
-// max / sum with the lane 32 apart (v_permlane32_swap).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Lazy-rescale online softmax of the two column tiles; returns the
-// wave-uniform "rescale O" flag, the per-column factors and the bf16 P.
-__device__ __forceinline__ bool softmax_lazy(f32x16 (&s)[2][2], float (&m)[2], float (&l)[2],
-                                             float (&alpha)[2], u32x4 (&p)[2][2][2], float c2) {
-  float mx[2];
+// Move the running max (and rescale O, l) when a slice max exceeds it by
+// more than kTau; wave-uniform branch, taken rarely.
+template <int QT, int DT>
+__device__ __forceinline__ void rescale_top(const float (&mx)[QT], float (&m)[QT], float (&l)[QT],
+                                            f32x16 (&o)[QT][DT], float c2) {
   bool need = false;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float x = fmaxf(s[qt][0][0], s[qt][1][0]);
+  for (int qt = 0; qt < QT; ++qt) need |= (mx[qt] - m[qt]) * c2 > kTau;
+  if (__any(need)) {
 #pragma unroll
-    for (int i = 1; i < 16; ++i) x = fmaxf(x, fmaxf(s[qt][0][i], s[qt][1][i]));
-    x = pair_max(x);
-    mx[qt] = x;
-    need |= (x - m[qt]) * c2 > kTau;
+    for (int qt = 0; qt < QT; ++qt) {
+      const float m_new = fmaxf(m[qt], mx[qt]);
+      const float al = fast_exp2((m[qt] - m_new) * c2);
+      m[qt] = m_new;
+      l[qt] *= al;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= al;
+    }
   }
-  const bool any = __any(need);
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float m_new = any ? fmaxf(m[qt], mx[qt]) : m[qt];
-    alpha[qt] = fast_exp2((m[qt] - m_new) * c2);
-    m[qt] = m_new;
-    const float mc = m_new * c2;
-    float rs = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(fmaf(s[qt][kt][i], c2, -mc));
-        s[qt][kt][i] = e;
-        rs += e;
-      }
-    l[qt] = l[qt] * alpha[qt] + rs;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int b = kb * 8;
-        const f32x16& x = s[qt][kt];
-        p[qt][kt][kb] = u32x4{pack_bf16(x[b + 0], x[b + 1]), pack_bf16(x[b + 2], x[b + 3]),
-                              pack_bf16(x[b + 4], x[b + 5]), pack_bf16(x[b + 6], x[b + 7])};
-      }
-  }
-  return any;
 }
 
-template <int D, bool PHASE1>
-__global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
-  using Gm = Geo<D>;
+// exp2 + bf16 pack + row sum of the packed values (v_dot2c_f32_bf16), so l is
+// the sum of exactly the weights that enter P.V.
+template <int QT>
+__device__ __forceinline__ void slice_exp2(const f32x16 (&s)[QT], const float (&m)[QT],
+                                           float (&l)[QT], u32x4 (&p)[QT][2], float c2) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float mc = m[qt] * c2;
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int i = 8 * kb + 2 * h;
+        const uint32_t pk = pack_bf16(fast_exp2(fmaf(s[qt][i], c2, -mc)),
+                                      fast_exp2(fmaf(s[qt][i + 1], c2, -mc)));
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, rs, false);
+        w4[h] = pk;
+      }
+      p[qt][kb] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+    l[qt] += rs;
+  }
+}
+
+// One 64-key stage of the software-pipelined interior loop: slice (t,0)
+// then slice (t,1); the first QK of the next stage is issued in the second
+// half, after the ring barrier and the DMA of tile t + 3.
+template <int D, int NW, int QT, int ST>
+__device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, NW>& lo,
+                                               const u32x4 (&q)[QT][Geo<D, NW>::KS],
+                                               f32x16 (&sc)[QT], float (&mx)[QT], float (&m)[QT],
+                                               float (&l)[QT], f32x16 (&o)[QT][Geo<D, NW>::DT],
+                                               float c2, const char* Kt3, const char* Vt3, int w) {
+  using Gm = Geo<D, NW>;
+  rescale_top<QT, Gm::DT>(mx, m, l, o, c2);
+  {
+    f32x16 sn[QT];
+    u32x4 p[QT][2];
+    qk_slice<D, NW, QT, ST, 1>(smem, lo, q, sn);
+    slice_exp2<QT>(sc, m, l, p, c2);
+    pv_slice<D, NW, QT, ST, 0>(smem, lo, p, o);
+    slice_max3<QT>(sn, mx);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
+  }
+  rescale_top<QT, Gm::DT>(mx, m, l, o, c2);
+  wait_vmcnt<Gm::PER>();
+  __builtin_amdgcn_s_barrier();
+  dma_stage<D, NW, (ST + 3) & 3>(smem, Kt3, Vt3, lo, w);
+  {
+    f32x16 sn[QT];
+    u32x4 p[QT][2];
+    qk_slice<D, NW, QT, (ST + 1) & 3, 0>(smem, lo, q, sn);
+    slice_exp2<QT>(sc, m, l, p, c2);
+    pv_slice<D, NW, QT, ST, 1>(smem, lo, p, o);
+    slice_max3<QT>(sn, mx);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
+  }
+}
+
+// Wave -> columns: wave w owns QT column tiles of 32 (query row, head) pairs.
+// The workgroup covers 256 columns: HW heads of one kv head x 64*(4/HW) rows.
+template <int D, int NW, int QT, bool PHASE1>
+__global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
+  using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
-  using Tile = WideTile<D>;
-  static_assert(Tile::STAGE == Gm::STAGE, "stage geometry");
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * Gm::STAGE];
+  constexpr int WPR = 2 / QT;  // waves per 64-row sub-tile of one head
+  static_assert(NW * QT == 8, "workgroup covers 256 columns");
+  __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -432,7 +518,8 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
   const int64_t work = bid / a.NG;
   const int hq = gidx % a.HQ, t2 = gidx / a.HQ;
   const int kvh = t2 % a.Hkv, s = t2 / a.Hkv;
-  const int hw = w % a.HW, rw = w / a.HW;
+  const int wsub = w % WPR, wh = w / WPR;  // 32*QT-row piece, (head, 64-row sub-tile)
+  const int hw = wh % a.HW, rw = wh / a.HW;
   const int head = kvh * a.G + hq * a.HW + hw;
 
   int64_t row0, row_end, hiA = 0, loB, hiB, pos_off;
@@ -466,16 +553,16 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
                &hiB, &host);
     pos_off = a.kv_len - a.q_tokens;
   }
-  const int64_t wrow0 = row0 + rw * 64;  // this wave's first query row
+  const int64_t wrow0 = row0 + rw * 64 + wsub * 32 * QT;  // this wave's first query row
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
   const uint16_t* K = a.k + head_row0 * D;
   const uint16_t* V = a.v + head_row0 * D;
   const float c2 = a.c2;
 
   // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g
-  u32x4 qop[2][KS];
+  u32x4 qop[QT][KS];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int64_t r = wrow0 + 32 * qt + l32;
     const bool ok = r < row_end;
     const uint16_t* qp = a.q + (((int64_t)s * a.q_tokens + (ok ? r : 0)) * a.Hq + head) * D;
@@ -484,12 +571,17 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
       qop[qt][ks] = ok ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 oacc[2][DT];
+  f32x16 oacc[QT][DT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x16{};
-  float m[2] = {kMinit, kMinit}, l[2] = {0.0f, 0.0f};
+  float m[QT], l[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = kMinit;
+    l[qt] = 0.0f;
+  }
 
   // ---- tile classes. Range A: anchor [0, hiA), no mask. Range B: [loB, hiB),
   // causal (key <= query position). Interior tiles need no mask at all.
@@ -509,37 +601,38 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
     if (i1 < i0) i1 = i0;
   }
   const int n_int = nAi + (int)(i1 - i0);
-  auto int_kbase = [&](int j) -> int64_t {
+  // interior tile j -> byte offset of its rows (clamped to the last tile)
+  auto tile_off = [&](int j) -> int64_t {
     j = j < n_int ? j : n_int - 1;
-    return j < nAi ? (int64_t)j * 64 : (i0 + (j - nAi)) * 64;
+    return (j < nAi ? (int64_t)j * 64 : (i0 + (j - nAi)) * 64) * (int64_t)Gm::RB;
   };
 
   if (n_int > 0) {
-#pragma unroll
-    for (int j = 0; j < kStages - 1; ++j) dma_tile<D>(smem + j * Gm::STAGE, K, V, int_kbase(j), w, lane);
+    LaneOffsets<D, NW> lo;
+    lo.init(l32, g, w, lane);
+    const char* Kc = (const char*)K;
+    const char* Vc = (const char*)V;
+    dma_stage<D, NW, 0>(smem, Kc + tile_off(0), Vc + tile_off(0), lo, w);
+    dma_stage<D, NW, 1>(smem, Kc + tile_off(1), Vc + tile_off(1), lo, w);
+    dma_stage<D, NW, 2>(smem, Kc + tile_off(2), Vc + tile_off(2), lo, w);
     wait_vmcnt<2 * Gm::PER>();
     __builtin_amdgcn_s_barrier();
-    f32x16 sc[2][2];
-    qk_tile<D>(smem, qop, sc, l32, g);
-    for (int t = 0; t < n_int; ++t) {
-      wait_vmcnt<Gm::PER>();
-      __builtin_amdgcn_s_barrier();
-      dma_tile<D>(smem + ((t + 3) & 3) * Gm::STAGE, K, V, int_kbase(t + 3), w, lane);
-      f32x16 sn[2][2];
-      qk_tile<D>(smem + ((t + 1) & 3) * Gm::STAGE, qop, sn, l32, g);
-      float alpha[2];
-      u32x4 p[2][2][2];
-      if (softmax_lazy(sc, m, l, alpha, p, c2)) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha[qt];
-      }
-      pv_tile<D>(smem + (t & 3) * Gm::STAGE, p, oacc, l32, g);
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sc[qt][kt] = sn[qt][kt];
+    f32x16 sc[QT];
+    float mx[QT];
+    qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
+    slice_max3<QT>(sc, mx);
+    for (int t = 0; t < n_int; t += 4) {
+      interior_stage<D, NW, QT, 0>(smem, lo, qop, sc, mx, m, l, oacc, c2, Kc + tile_off(t + 3),
+                                   Vc + tile_off(t + 3), w);
+      if (t + 1 >= n_int) break;
+      interior_stage<D, NW, QT, 1>(smem, lo, qop, sc, mx, m, l, oacc, c2, Kc + tile_off(t + 4),
+                                   Vc + tile_off(t + 4), w);
+      if (t + 2 >= n_int) break;
+      interior_stage<D, NW, QT, 2>(smem, lo, qop, sc, mx, m, l, oacc, c2, Kc + tile_off(t + 5),
+                                   Vc + tile_off(t + 5), w);
+      if (t + 3 >= n_int) break;
+      interior_stage<D, NW, QT, 3>(smem, lo, qop, sc, mx, m, l, oacc, c2, Kc + tile_off(t + 6),
+                                   Vc + tile_off(t + 6), w);
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -547,49 +640,53 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(const WideArgs a) {
 
   // ---- edge tiles: masked, synchronous, staged through registers with zero fill
   const int n_edge = (a_edge ? 1 : 0) + (int)(i0 - bf) + (int)(bl - i1);
-  for (int e = 0; e < n_edge; ++e) {
-    int64_t kbase, lo, hi;
-    bool causal;
-    int k = e;
-    if (a_edge && k == 0) {
-      kbase = (int64_t)nAi * 64; lo = 0; hi = hiA; causal = false;
-    } else {
-      k -= a_edge ? 1 : 0;
-      kbase = (k < i0 - bf ? bf + k : i1 + (k - (i0 - bf))) * 64;
-      lo = loB; hi = hiB; causal = true;
-    }
-    Tile st;
-    st.load(K, V, kbase, lo, hi, tid);
-    st.store(smem, tid);
-    block_sync_lds();
-    f32x16 sc[2][2];
-    qk_tile<D>(smem, qop, sc, l32, g);
+  if (n_edge > 0) {
+    LaneOffsets<D, NW> lo;
+    lo.init(l32, g, w, lane);
+    for (int e = 0; e < n_edge; ++e) {
+      int64_t kbase, klo, khi;
+      bool causal;
+      int k = e;
+      if (a_edge && k == 0) {
+        kbase = (int64_t)nAi * 64; klo = 0; khi = hiA; causal = false;
+      } else {
+        k -= a_edge ? 1 : 0;
+        kbase = (k < i0 - bf ? bf + k : i1 + (k - (i0 - bf))) * 64;
+        klo = loB; khi = hiB; causal = true;
+      }
+      EdgeTile<D, NW> et;
+      et.load(K, V, kbase, klo, khi, tid);
+      et.store(smem, tid);
+      block_sync_lds();
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int64_t pos = wrow0 + 32 * qt + l32 + pos_off;
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 sc[QT];
+        if (kt == 0) qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
+        else qk_slice<D, NW, QT, 0, 1>(smem, lo, qop, sc);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int qt = 0; qt < QT; ++qt) {
+          const int64_t pos = wrow0 + 32 * qt + l32 + pos_off;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = kbase + 32 * kt + acc_key(i, g);
-          if (key < lo || key >= hi || (causal && key > pos)) sc[qt][kt][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int64_t key = kbase + 32 * kt + acc_key(i, g);
+            if (key < klo || key >= khi || (causal && key > pos)) sc[qt][i] = -INFINITY;
+          }
         }
+        float mx[QT];
+        slice_max3<QT>(sc, mx);
+        rescale_top<QT, DT>(mx, m, l, oacc, c2);
+        u32x4 p[QT][2];
+        slice_exp2<QT>(sc, m, l, p, c2);
+        if (kt == 0) pv_slice<D, NW, QT, 0, 0>(smem, lo, p, oacc);
+        else pv_slice<D, NW, QT, 0, 1>(smem, lo, p, oacc);
+      }
+      block_sync_lds();
     }
-    float alpha[2];
-    u32x4 p[2][2][2];
-    if (softmax_lazy(sc, m, l, alpha, p, c2)) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha[qt];
-    }
-    pv_tile<D>(smem, p, oacc, l32, g);
-    block_sync_lds();
   }
 
   // ---- epilogue: accumulator element i of tile dt is dimension 32*dt + 8*(i/4) + 4*g + i%4
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const float lt = pair_sum(l[qt]);
     const int64_t r = wrow0 + 32 * qt + l32;
     if (r >= row_end) continue;
@@ -958,6 +1055,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
 
+// Waves per wide-kernel workgroup: 8 (two per SIMD, 32 columns each) or 4
+// (one per SIMD, 64 columns each).
+#ifndef STAR_WIDE_WAVES
+#define STAR_WIDE_WAVES 8
+#endif
+constexpr int kWideWaves = STAR_WIDE_WAVES;
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1041,8 +1145,12 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
   a.c2 = d.scale_log2;
   const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
   const dim3 grid((unsigned)nwg);
-  if (d.D == 128) hipLaunchKernelGGL((attn_wide_kernel<128, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_wide_kernel<64, true>), grid, dim3(256), 0, st, a);
+  if (d.D == 128)
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true>), grid,
+                       dim3(64 * kWideWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true>), grid,
+                       dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
 
@@ -1122,8 +1230,12 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
   a.scale = d.scale;
   a.c2 = d.scale_log2;
   const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
-  if (d.D == 128) hipLaunchKernelGGL((attn_wide_kernel<128, false>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_wide_kernel<64, false>), grid, dim3(256), 0, st, a);
+  if (d.D == 128)
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false>), grid,
+                       dim3(64 * kWideWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false>), grid,
+                       dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
 
