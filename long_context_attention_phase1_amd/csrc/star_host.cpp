@@ -64,12 +64,15 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
   p.narrow = (d.dtype != STAR_BF16) || cols <= kNarrowCols;
   p.n_groups = p.narrow ? d.B * d.Hkv : d.B * d.Hkv * d.HQ;
   p.n_qtiles = p.narrow ? 1 : (int32_t)cdiv(n_query, (int64_t)kColsPerWave * d.RW);
-  int64_t target = kTargetWorkgroups / ((int64_t)p.n_groups * p.n_qtiles);
+  // decode: ~one long-running workgroup per CU; many query rows: 8 per CU
+  const int64_t total = p.narrow ? kNarrowWorkgroups : kTargetWorkgroups;
+  const int64_t min_len = p.narrow ? 512 : 256;
+  int64_t target = total / ((int64_t)p.n_groups * p.n_qtiles);
   if (target < 1) target = 1;
   // splits per context block: proportional to the block's share of the cache,
-  // no split shorter than 256 rows
+  // no split shorter than min_len rows
   int64_t per = (int64_t)llround((double)target * (double)d.blk / (double)kv_len);
-  const int64_t max_per = d.blk / 256;
+  const int64_t max_per = d.blk / min_len;
   if (per > max_per) per = max_per;
   if (per <= 1) {
     p.per_block = 1;
@@ -79,7 +82,8 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
     p.per_block = (int32_t)cdiv(d.blk, p.blk_len);
   }
   const int64_t tail = kv_len - d.L;
-  const int64_t tl_target = p.per_block > 1 ? p.blk_len : (d.blk > 256 ? round_up(d.blk, kTile) : 256);
+  const int64_t tl_target =
+      p.per_block > 1 ? p.blk_len : (d.blk > min_len ? round_up(d.blk, kTile) : min_len);
   p.tail_splits = (int32_t)cdiv(tail, tl_target);
   p.tail_len = p.tail_splits == 1 ? tail : round_up(cdiv(tail, p.tail_splits), kTile);
   p.n_split = d.n_blocks * p.per_block + p.tail_splits;

@@ -12,7 +12,8 @@ constexpr int kTile = STAR_KV_TILE;   // rows of a KV-cache tile
 constexpr int kWaves = 4;             // waves per workgroup of the MFMA kernels
 constexpr int kColsPerWave = 64;      // query columns (row, head pairs) per wave
 constexpr int kNarrowCols = 32;       // columns of the single-tile decode kernel
-constexpr int kTargetWorkgroups = 2048;  // phase-2 split planner target (8 per CU)
+constexpr int kTargetWorkgroups = 2048;  // phase-2 planner target, many query rows (8 per CU)
+constexpr int kNarrowWorkgroups = 256;   // phase-2 planner target, decode (one per CU)
 
 // Everything derived from a validated descriptor.
 struct Dims {

@@ -26,6 +26,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "star_internal.hpp"
 
 namespace star {
@@ -740,18 +742,57 @@ struct NarrowArgs {
   float scale, c2;
 };
 
+// One decode iteration: wait for the pair of tiles in stages (2*PI, 2*PI+1),
+// compute this wave's slice, then refill those stages with the pair after next.
+template <int D, int PI>
+__device__ __forceinline__ void narrow_iteration(
+    char* smem, const LaneOffsets<D, 4>& lo4, const uint32_t (&kq)[Geo<D, 4>::KS],
+    const uint32_t (&vq)[2], const u32x4 (&qop)[1][Geo<D, 4>::KS],
+    f32x16 (&oacc)[1][Geo<D, 4>::DT], float (&m)[1], float (&l)[1], float c2, bool active,
+    const char* Ka, const char* Va, const char* Kb, const char* Vb, int w) {
+  using Gm = Geo<D, 4>;
+  wait_vmcnt<2 * Gm::PER>();
+  __builtin_amdgcn_s_barrier();
+  if (active) {
+    f32x16 sc[1];
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks)
+      sc[0] = mfma_bf16(lds16(smem + kq[ks] + PI * 2 * Gm::KBYTES), qop[0][ks],
+                        ks == 0 ? f32x16{} : sc[0]);
+    float mx[1];
+    slice_max3<1>(sc, mx);
+    rescale_top<1, Gm::DT>(mx, m, l, oacc, c2);
+    u32x4 p[1][2];
+    slice_exp2<1>(sc, m, l, p, c2);
+#pragma unroll
+    for (int dt = 0; dt < Gm::DT; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        oacc[0][dt] = mfma_bf16(lds16(smem + vq[kb] + (PI * 2 * Gm::VBYTES + dt * 32 * 128)),
+                                p[0][kb], oacc[0][dt]);
+  }
+  block_sync_lds();
+  dma_stage<D, 4, 2 * PI>(smem, Ka, Va, lo4, w);
+  dma_stage<D, 4, 2 * PI + 1>(smem, Kb, Vb, lo4, w);
+}
+
+// Decode partial kernel. One workgroup per (sequence, kv head, split); the
+// split's interior 64-key tiles stream through a ring of four LDS stages by
+// direct-to-LDS loads, two tiles per iteration, the next iteration's two in
+// flight. Waves 0,1 take the 32-key slices of the even tile, waves 2,3 those
+// of the odd tile, each with its own softmax state; the four states are
+// merged through LDS at the end. Sized so ~one workgroup per CU streams a
+// long contiguous key range with ~128 KB of loads outstanding.
 template <int D>
 __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
-  constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
-  constexpr int KBYTES = 128 * D * 2;     // 128 K rows
-  constexpr int VTBYTES = D * 128;        // one transposed 64-key V tile
-  constexpr int KPT = 128 * CH / 256, VPT = 2 * D * 8 / 256;
-  constexpr int SMEM = KBYTES + 2 * VTBYTES;
-  static_assert(SMEM >= 4 * 32 * D * 4, "merge area must fit");
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  using Gm = Geo<D, 4>;
+  constexpr int KS = Gm::KS, DT = Gm::DT;
+  static_assert(Gm::RING >= 4 * 32 * D * 4, "merge area must fit in the ring");
+  __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
   __shared__ float msm[4][32], lsm[4][32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
+  const int tp = w >> 1, kt = w & 1;  // tile of the pair, 32-key slice of the tile
 
   const int gidx = (int)(blockIdx.x % a.NG);
   const int32_t sigma = (int32_t)(blockIdx.x / a.NG);
@@ -770,90 +811,110 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
   const uint16_t* K = a.k + head_row0 * D;
   const uint16_t* V = a.v + head_row0 * D;
+  const float c2 = a.c2;
 
-  u32x4 qop[KS];
+  u32x4 qop[1][KS];
   {
     const uint16_t* qp = a.q + (((int64_t)s * a.n_query + (cvalid ? cj : 0)) * a.Hq + ch) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[ks] = cvalid ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks)
+      qop[0][ks] = cvalid ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
   }
-  f32x16 oacc[DT];
+  f32x16 oacc[1][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m = kMinit, l = 0.0f;
+  for (int dt = 0; dt < DT; ++dt) oacc[0][dt] = f32x16{};
+  float m[1] = {kMinit}, l[1] = {0.0f};
 
-  const int64_t kb0 = (lo / 64) * 64;
-  const int nS = hi > lo ? (int)cdiv64(hi - kb0, 128) : 0;
-  u32x4 kr[KPT], vr[VPT];
-  auto load = [&](int64_t kbase) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 256 * i, slot = u / CH, c = u % CH;
-      const int64_t key = kbase + (slot & ~31) + swap23(slot & 31);
-      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + 256 * i, vt = u / (D * 8), rem = u % (D * 8), e = rem >> 3, kc = rem & 7;
-      const int64_t tb = kbase + 64 * vt;
-      vr[i] = load_v_chunk(V + tb * D + e * 64 + kc * 8, tb + kc * 8, lo, hi);
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 256 * i;
-      sts16(smem + k_off<D>(u / CH, u % CH), kr[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + 256 * i, vt = u / (D * 8), rem = u % (D * 8);
-      sts16(smem + KBYTES + vt * VTBYTES + v_off(rem >> 3, rem & 7), vr[i]);
-    }
-  };
+  // interior tiles: inside [lo, hi) and not after any query position
+  int64_t bf = 0, bl = 0, i0 = 0, i1 = 0;
+  if (hi > lo) {
+    bf = lo / 64;
+    bl = cdiv64(hi, 64);
+    int64_t t1 = hi / 64;
+    const int64_t tpz = (pos0 + 1) / 64;
+    if (tpz < t1) t1 = tpz;
+    const int64_t t0 = cdiv64(lo, 64);
+    i0 = t0 > bf ? t0 : bf;
+    i1 = t1 < bl ? t1 : bl;
+    if (i1 < i0) i1 = i0;
+  }
+  const int n_int = (int)(i1 - i0);
 
-  if (nS > 0) {
-    load(kb0);
-    store();
-    __syncthreads();
-    for (int t = 0; t < nS; ++t) {
-      const int64_t kbase = kb0 + (int64_t)t * 128;
-      if (t + 1 < nS) load(kbase + 128);
-      const int64_t wk = kbase + 32 * w;  // first key of this wave's slice
-      if (wk < hi && wk + 32 > lo) {
-        f32x16 sacc[1] = {f32x16{}};
+  if (n_int > 0) {
+    LaneOffsets<D, 4> lo4;
+    lo4.init(l32, g, w, lane);
+    // this wave's operand offsets: its tile of the pair and its slice
+    uint32_t kq[KS], vq[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kq[ks] = lo4.kq[ks] + tp * Gm::KBYTES + kt * 32 * Gm::RB;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      vq[kb] = (uint32_t)(Gm::V_AT + tp * Gm::VBYTES) + v_off(l32, 4 * kt + 2 * kb + g);
+    const char* Kc = (const char*)K;
+    const char* Vc = (const char*)V;
+    const int64_t base_off = i0 * 64 * (int64_t)Gm::RB;
+    const int jmax = n_int - 1;
+#define STAR_TOFF(j) (base_off + (int64_t)((j) < jmax ? (j) : jmax) * 64 * Gm::RB)
+    const int n_it = (n_int + 1) / 2;
+    dma_stage<D, 4, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
+    dma_stage<D, 4, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
+    dma_stage<D, 4, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
+    dma_stage<D, 4, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
+    for (int it = 0; it < n_it; it += 2) {
+      narrow_iteration<D, 0>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + tp < n_int,
+                             Kc + STAR_TOFF(2 * it + 4), Vc + STAR_TOFF(2 * it + 4),
+                             Kc + STAR_TOFF(2 * it + 5), Vc + STAR_TOFF(2 * it + 5), w);
+      if (it + 1 >= n_it) break;
+      narrow_iteration<D, 1>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + 2 + tp < n_int,
+                             Kc + STAR_TOFF(2 * it + 6), Vc + STAR_TOFF(2 * it + 6),
+                             Kc + STAR_TOFF(2 * it + 7), Vc + STAR_TOFF(2 * it + 7), w);
+    }
+#undef STAR_TOFF
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // edge tiles (the causal tail, unaligned ends): waves 0,1, masked
+  const int n_edge = (int)(i0 - bf) + (int)(bl - i1);
+  if (n_edge > 0) {
+    for (int e = 0; e < n_edge; ++e) {
+      const int64_t kbase = (e < i0 - bf ? bf + e : i1 + (e - (i0 - bf))) * 64;
+      EdgeTile<D, 4> et;
+      et.load(K, V, kbase, lo, hi, tid);
+      et.store(smem, tid);
+      block_sync_lds();
+      if (tp == 0) {
+        f32x16 sc[1];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          sacc[0] = mfma_bf16(lds16(smem + k_off<D>(32 * w + l32, 2 * ks + g)), qop[ks], sacc[0]);
-        if (wk < lo || wk + 32 > hi || wk + 31 > pos0 || !cvalid) {
+          sc[0] = mfma_bf16(lds16(smem + k_off<D>(l32, 2 * ks + g) + kt * 32 * Gm::RB),
+                            qop[0][ks], ks == 0 ? f32x16{} : sc[0]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t key = wk + acc_key(i, g);
-            if (key < lo || key >= hi || key > cpos || !cvalid) sacc[0][i] = -INFINITY;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int64_t key = kbase + 32 * kt + acc_key(i, g);
+          if (key < lo || key >= hi || key > cpos || !cvalid) sc[0][i] = -INFINITY;
         }
+        float mx[1];
+        slice_max3<1>(sc, mx);
+        rescale_top<1, DT>(mx, m, l, oacc, c2);
         u32x4 p[1][2];
-        softmax_update<1, DT>(sacc, m, l, oacc, p, a.c2);
-        const char* vbase = smem + KBYTES + (w >> 1) * VTBYTES;
+        slice_exp2<1>(sc, m, l, p, c2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            oacc[dt] = mfma_bf16(lds16(vbase + v_off(32 * dt + l32, 4 * (w & 1) + 2 * kb + g)),
-                                 p[0][kb], oacc[dt]);
+            oacc[0][dt] = mfma_bf16(
+                lds16(smem + Gm::V_AT + v_off(l32, 4 * kt + 2 * kb + g) + dt * 32 * 128), p[0][kb],
+                oacc[0][dt]);
       }
-      __syncthreads();
-      if (t + 1 < nS) {
-        store();
-        __syncthreads();
-      }
+      block_sync_lds();
     }
   }
 
   // ---- merge the four waves' (m, l, O) and write the split's partial
-  const float lw = l + __shfl_xor(l, 32, 64);
+  const float lw = pair_sum(l[0]);
   if (g == 0) {
-    msm[w][l32] = m;
+    msm[w][l32] = m[0];
     lsm[w][l32] = lw;
   }
   float* osm = (float*)smem;  // [4][32][D]
@@ -861,7 +922,7 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oacc[dt][i];
+      osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oacc[0][dt][i];
   __syncthreads();
   for (int idx = tid; idx < 32 * D; idx += 256) {
     const int c = idx / D, e = idx % D;
@@ -872,7 +933,7 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     float Ls = 0.0f, O = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2((msm[ww][c] - M) * a.c2);
+      const float f = fast_exp2((msm[ww][c] - M) * c2);
       Ls += f * lsm[ww][c];
       O += f * osm[(ww * 32 + c) * D + e];
     }

@@ -40,7 +40,7 @@ CASES = {
     # tail longer than one split: early query rows see nothing of the second tail split
     "long_tail_wide": W("long_tail", 1, 4, 2, 128, 128, 64, 64, 300, 1, "bf16", seed=13),
     # last block shorter than the split length: its second split is empty
-    "ragged_empty_split": W("ragged_empty", 1, 4, 1, 128, 1100, 512, 300, 2, 2, "bf16", seed=14),
+    "ragged_empty_split": W("ragged_empty", 1, 4, 1, 128, 2100, 1024, 300, 2, 2, "bf16", seed=14),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
