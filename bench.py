@@ -156,16 +156,17 @@ def main():
         for t in range(w.n_decode):
             row = w.n_query + t
             kv_len = w.ctx_len + row + 1
-            sa.star_kv_write(p.desc, p.k_cache, p.v_cache, w.ctx_len + row, p.k_tail_rows[row],
-                             p.v_tail_rows[row], 1)
             n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
-            k0, k1 = ev(), ev()
-            k0.record(stream)
-            sa.star_attn_phase2_partial(p.desc, p.k_cache, p.v_cache, kv_len,
-                                        p.q_tail_rows[row], 1, o_part, lse_part)
-            k1.record(stream)
-            sa.star_attn_lse_merge(p.desc, 1, n_split, o_part, lse_part, o, p.dtype, lse)
             if record:
+                k0 = ev()
+                k0.record(stream)
+            # append the token's K/V + split partials (one launch), then the merge
+            sa.star_attn_decode_step(p.desc, p.k_cache, p.v_cache, kv_len, p.q_tail_rows[row],
+                                     p.k_tail_rows[row], p.v_tail_rows[row], 1, o_part, lse_part,
+                                     o, p.dtype, lse)
+            if record:
+                k1 = ev()
+                k1.record(stream)
                 dec_events.append((k0, k1))
                 dec_bytes.append(decode_bytes(w, kv_len, n_split))
         d1 = ev()
@@ -200,7 +201,7 @@ def main():
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
     kname1 = "attn_wide_kernel<128,phase1>"
-    kname2 = "attn_narrow_kernel<128>"
+    kname2 = "attn_narrow_kernel<128,fused>"
     t1, t2 = load_traffic(kname1), load_traffic(kname2)
     out = {
         "metric": METRIC,
@@ -233,7 +234,8 @@ def main():
         "roofline_phase2": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS, "traffic": t2,
                             "kernel": kname2,
-                            "algorithmic": "K+V rows [0, kv_len) + q + fp32 partials per launch"},
+                            "algorithmic": "K+V rows [0, kv_len) + q + fp32 partials per launch "
+                                           "(one fused decode-step launch: append, partials, merge)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)

@@ -186,6 +186,25 @@ int star_attn_lse_merge(const star_attn_desc* desc, int64_t n_query, int32_t n_s
                         const float* o_part, const float* lse_part, void* o, int32_t o_dtype,
                         float* lse_out, void* stream);
 
+/*
+ * star_attn_decode_step - one step of the query host's autoregressive loop
+ * (podcast, Phase 2 description: append the new token's KV to the cache,
+ * gather every host's vector and scalar, aggregate):
+ *   1. writes k_new / v_new ([batch][n_query][n_kv_heads][head_dim], desc->dtype)
+ *      into cache rows [kv_len - n_query, kv_len);
+ *   2. computes the split partials exactly as star_attn_phase2_partial
+ *      (o_part, lse_part laid out as there, n_split from star_attn_phase2_plan);
+ *   3. merges them exactly as star_attn_lse_merge into o / lse_out.
+ * When n_query * (n_q_heads / n_kv_heads) <= 32 and dtype is bf16, steps 1
+ * and 2 are one kernel launch (the split that owns the new rows writes them
+ * before reading them) and step 3 a second; otherwise three launches.
+ * Argument checks as the three separate calls.
+ */
+int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cache,
+                          int64_t kv_len, const void* q, const void* k_new, const void* v_new,
+                          int64_t n_query, float* o_part, float* lse_part, void* o,
+                          int32_t o_dtype, float* lse_out, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* star_attn_strerror(int status);
 

@@ -31,7 +31,7 @@ STAR_KV_TILE = 64
 
 EXPORTS = ("star_kv_cache_bytes", "star_kv_write", "star_attn_phase1", "star_attn_phase2_plan",
            "star_attn_phase2_split_range", "star_attn_phase2_partial", "star_attn_lse_merge",
-           "star_attn_strerror", "star_attn_abi_version")
+           "star_attn_decode_step", "star_attn_strerror", "star_attn_abi_version")
 
 
 class StarAttnError(RuntimeError):
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                         ctypes.POINTER(I64), ctypes.POINTER(I32)]),
         "star_attn_phase2_partial": (ctypes.c_int, [D, P, P, I64, P, I64, P, P, P]),
         "star_attn_lse_merge": (ctypes.c_int, [D, I64, I32, P, P, P, I32, P, P]),
+        "star_attn_decode_step": (ctypes.c_int, [D, P, P, I64, P, P, P, I64, P, P, P, I32, P, P]),
         "star_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "star_attn_abi_version": (ctypes.c_int, []),
     }
@@ -227,3 +228,21 @@ def star_attn_lse_merge(desc, n_query: int, n_split: int, o_part, lse_part, o, o
         _ptr(lse_part, shp_o[:3] + (n_split,), f32, "lse_part"), _ptr(o, shp_o, od, "o"), o_dtype,
         _ptr(lse_out, shp_o[:3], f32, "lse_out"), _stream(stream))
     _check(st, "star_attn_lse_merge")
+
+
+def star_attn_decode_step(desc, k_cache, v_cache, kv_len: int, q, k_new, v_new, n_query: int,
+                          o_part, lse_part, o, o_dtype: int, lse_out=None, stream=None):
+    torch = None if isinstance(q, int) else _torch()
+    n_split = star_attn_phase2_plan(desc, kv_len, n_query)
+    shp_q = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    shp_kv = (desc.batch, n_query, desc.n_kv_heads, desc.head_dim)
+    shp_p = (desc.batch, n_query, desc.n_q_heads, n_split, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    elt = None if torch is None else _elt(desc)
+    od = None if torch is None else (torch.bfloat16 if o_dtype == STAR_BF16 else torch.float32)
+    st = load_library().star_attn_decode_step(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        kv_len, _ptr(q, shp_q, elt, "q"), _ptr(k_new, shp_kv, elt, "k_new"),
+        _ptr(v_new, shp_kv, elt, "v_new"), n_query, _ptr(o_part, shp_p, f32, "o_part"),
+        _ptr(lse_part, shp_p[:4], f32, "lse_part"), _ptr(o, shp_q, od, "o"), o_dtype, _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
+    _check(st, "star_attn_decode_step")

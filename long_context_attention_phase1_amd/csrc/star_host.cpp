@@ -174,6 +174,30 @@ int star_attn_lse_merge(const star_attn_desc* desc, int64_t n_query, int32_t n_s
   return launch_lse_merge(d, n_query, n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }
 
+int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cache,
+                          int64_t kv_len, const void* q, const void* k_new, const void* v_new,
+                          int64_t n_query, float* o_part, float* lse_part, void* o,
+                          int32_t o_dtype, float* lse_out, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !q || !k_new || !v_new || !o_part || !lse_part || !o)
+    return STAR_ERR_INVALID_ARG;
+  if (o_dtype != STAR_BF16 && o_dtype != STAR_F32) return STAR_ERR_DTYPE;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  if (p.narrow && d.dtype == STAR_BF16)
+    return launch_decode_step(d, p, k_cache, v_cache, kv_len, q, k_new, v_new, n_query, o_part,
+                              lse_part, o, o_dtype, lse_out, stream);
+  // many query columns or fp32: the same three steps as separate launches
+  st = launch_kv_write(d, k_cache, v_cache, kv_len - n_query, k_new, v_new, n_query, stream);
+  if (st) return st;
+  st = launch_phase2_partial(d, p, k_cache, v_cache, kv_len, q, n_query, o_part, lse_part, stream);
+  if (st) return st;
+  return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
+}
+
 const char* star_attn_strerror(int status) {
   switch (status) {
     case STAR_OK: return "success";

@@ -86,6 +86,10 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
 int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
                           int64_t kv_len, const void* q, int64_t n_query, float* o_part,
                           float* lse_part, void* stream);
+int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
+                       const void* q, const void* k_new, const void* v_new, int64_t n_query,
+                       float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
+                       void* stream);
 int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const float* o_part,
                      const float* lse_part, void* o, int32_t o_dtype, float* lse_out,
                      void* stream);

@@ -377,6 +377,42 @@ __device__ __forceinline__ void dma_stage(char* smem, const char* Kt, const char
                                                  (Gm::VI * w + j) * 1024), 16, 0, 0);
 }
 
+// The same loads as dma_stage, issued through a minimal asm statement. The
+// compiler then keeps no record of them as LDS writes and inserts no drain of
+// the load counter before the next LDS reads; the caller waits with explicit
+// vmcnt and a barrier before reading a stage (the asm has no register
+// outputs: the data lands in LDS).
+//
+// The compiler's hazard recognizer does not look inside asm, so the asm
+// supplies the wait states itself: an SALU write of M0 needs one before an
+// LDS DMA reads it, a VALU write of an SGPR (v_readfirstlane) five before a
+// VMEM instruction reads it; s_nop 4 gives five.
+__device__ __forceinline__ void dma16_lds(const char* gbase, uint32_t voff, const char* lds) {
+  // the base is wave-uniform: pin it to an SGPR pair for the saddr operand.
+  // readfirstlane returns int: go through uint32_t so the low half is
+  // zero-extended, not sign-extended into the high half
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase;
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gb);
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gb >> 32));
+  const uint64_t gs = ((uint64_t)ghi << 32) | (uint64_t)glo;
+  const uint32_t m0 =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gs), "{m0}"(m0)
+               : "memory");
+}
+
+template <int D, int NW, int ST>
+__device__ __forceinline__ void dma_stage_asm(char* smem, const char* Kt, const char* Vt,
+                                              const LaneOffsets<D, NW>& lo, int w) {
+  using Gm = Geo<D, NW>;
+#pragma unroll
+  for (int j = 0; j < Gm::KI; ++j)
+    dma16_lds(Kt, lo.kd[j], smem + Gm::K_AT + ST * Gm::KBYTES + (Gm::KI * w + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < Gm::VI; ++j)
+    dma16_lds(Vt, lo.vd[j], smem + Gm::V_AT + ST * Gm::VBYTES + (Gm::VI * w + j) * 1024);
+}
+
 // S^T of one 32-key slice KT of stage ST for the QT column tiles.
 template <int D, int NW, int QT, int ST, int KT>
 __device__ __forceinline__ void qk_slice(const char* smem, const LaneOffsets<D, NW>& lo,
@@ -740,6 +776,9 @@ struct NarrowArgs {
   int32_t per_block, n_split, n_blocks;
   int32_t Hq, Hkv, G, NG;
   float scale, c2;
+  // decode step (FUSED kernels only): rows appended at kv_len - n_query
+  const uint16_t* k_new;  // [B][n_query][Hkv][D]
+  const uint16_t* v_new;
 };
 
 // One decode iteration: wait for the pair of tiles in stages (2*PI, 2*PI+1),
@@ -753,27 +792,28 @@ __device__ __forceinline__ void narrow_iteration(
   using Gm = Geo<D, 4>;
   wait_vmcnt<2 * Gm::PER>();
   __builtin_amdgcn_s_barrier();
-  if (active) {
-    f32x16 sc[1];
+  // branch-free: a wave without a tile this iteration (odd tile count) reads
+  // the clamped duplicate tile and masks every score, leaving its state as is
+  f32x16 sc[1];
 #pragma unroll
-    for (int ks = 0; ks < Gm::KS; ++ks)
-      sc[0] = mfma_bf16(lds16(smem + kq[ks] + PI * 2 * Gm::KBYTES), qop[0][ks],
-                        ks == 0 ? f32x16{} : sc[0]);
-    float mx[1];
-    slice_max3<1>(sc, mx);
-    rescale_top<1, Gm::DT>(mx, m, l, oacc, c2);
-    u32x4 p[1][2];
-    slice_exp2<1>(sc, m, l, p, c2);
+  for (int ks = 0; ks < Gm::KS; ++ks)
+    sc[0] = mfma_bf16(lds16(smem + kq[ks] + PI * 2 * Gm::KBYTES), qop[0][ks],
+                      ks == 0 ? f32x16{} : sc[0]);
+  if (!active) sc[0] = f32x16{} - INFINITY;
+  float mx[1];
+  slice_max3<1>(sc, mx);
+  rescale_top<1, Gm::DT>(mx, m, l, oacc, c2);
+  u32x4 p[1][2];
+  slice_exp2<1>(sc, m, l, p, c2);
 #pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt)
+  for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        oacc[0][dt] = mfma_bf16(lds16(smem + vq[kb] + (PI * 2 * Gm::VBYTES + dt * 32 * 128)),
-                                p[0][kb], oacc[0][dt]);
-  }
+    for (int kb = 0; kb < 2; ++kb)
+      oacc[0][dt] = mfma_bf16(lds16(smem + vq[kb] + (PI * 2 * Gm::VBYTES + dt * 32 * 128)),
+                              p[0][kb], oacc[0][dt]);
   block_sync_lds();
-  dma_stage<D, 4, 2 * PI>(smem, Ka, Va, lo4, w);
-  dma_stage<D, 4, 2 * PI + 1>(smem, Kb, Vb, lo4, w);
+  dma_stage_asm<D, 4, 2 * PI>(smem, Ka, Va, lo4, w);
+  dma_stage_asm<D, 4, 2 * PI + 1>(smem, Kb, Vb, lo4, w);
 }
 
 // Decode partial kernel. One workgroup per (sequence, kv head, split); the
@@ -783,7 +823,7 @@ __device__ __forceinline__ void narrow_iteration(
 // of the odd tile, each with its own softmax state; the four states are
 // merged through LDS at the end. Sized so ~one workgroup per CU streams a
 // long contiguous key range with ~128 KB of loads outstanding.
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   using Gm = Geo<D, 4>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
@@ -794,8 +834,10 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const int tp = w >> 1, kt = w & 1;  // tile of the pair, 32-key slice of the tile
 
+  // splits in reverse order: the short, partly masked tail splits start first
+  // instead of waiting for a CU after the long context splits
   const int gidx = (int)(blockIdx.x % a.NG);
-  const int32_t sigma = (int32_t)(blockIdx.x / a.NG);
+  const int32_t sigma = a.n_split - 1 - (int32_t)(blockIdx.x / a.NG);
   const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
   int64_t lo, hi;
   int32_t host;
@@ -813,17 +855,40 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const uint16_t* V = a.v + head_row0 * D;
   const float c2 = a.c2;
 
-  u32x4 qop[1][KS];
-  {
-    const uint16_t* qp = a.q + (((int64_t)s * a.n_query + (cvalid ? cj : 0)) * a.Hq + ch) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[0][ks] = cvalid ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+  if (FUSED) {
+    // append: this split's share of the new rows [pos0, kv_len) goes into the
+    // cache before any of its tiles is loaded (no other split reads them)
+    const int64_t r0 = pos0 > lo ? pos0 : lo;
+    const int64_t r1 = a.kv_len < hi ? a.kv_len : hi;
+    if (r1 > r0) {
+      uint16_t* Kw = (uint16_t*)K;
+      uint16_t* Vw = (uint16_t*)V;
+      const int n = (int)(r1 - r0);
+      for (int u = tid; u < n * D; u += 256) {
+        const int rr = u / D, e = u % D;
+        const int64_t r = r0 + rr;
+        const int64_t src = (((int64_t)s * a.n_query + (r - pos0)) * a.Hkv + kvh) * D + e;
+        Kw[r * D + e] = a.k_new[src];
+        Vw[(r / 64) * 64 * D + e * 64 + (r % 64)] = a.v_new[src];
+      }
+      // the stores must complete before this workgroup loads those rows;
+      // every other split never reads them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+    }
   }
+
   f32x16 oacc[1][DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[0][dt] = f32x16{};
   float m[1] = {kMinit}, l[1] = {0.0f};
+
+  u32x4 qop[1][KS];
+  auto load_q = [&](u32x4 (&q)[1][KS]) {
+    const uint16_t* qp = a.q + (((int64_t)s * a.n_query + (cvalid ? cj : 0)) * a.Hq + ch) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q[0][ks] = cvalid ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+  };
 
   // interior tiles: inside [lo, hi) and not after any query position
   int64_t bf = 0, bl = 0, i0 = 0, i1 = 0;
@@ -856,10 +921,15 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     const int jmax = n_int - 1;
 #define STAR_TOFF(j) (base_off + (int64_t)((j) < jmax ? (j) : jmax) * 64 * Gm::RB)
     const int n_it = (n_int + 1) / 2;
-    dma_stage<D, 4, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
-    dma_stage<D, 4, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
-    dma_stage<D, 4, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
-    dma_stage<D, 4, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
+    dma_stage_asm<D, 4, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
+    dma_stage_asm<D, 4, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
+    dma_stage_asm<D, 4, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
+    dma_stage_asm<D, 4, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
+    load_q(qop);
+    // one drain before the loop (query and the first four tiles): the
+    // compiler then knows the query registers are complete and inserts no
+    // wait inside the loop
+    wait_vmcnt<0>();
     for (int it = 0; it < n_it; it += 2) {
       narrow_iteration<D, 0>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + tp < n_int,
                              Kc + STAR_TOFF(2 * it + 4), Vc + STAR_TOFF(2 * it + 4),
@@ -873,6 +943,8 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
   }
+
+  if (n_int == 0) load_q(qop);
 
   // edge tiles (the causal tail, unaligned ends): waves 0,1, masked
   const int n_edge = (int)(i0 - bf) + (int)(bl - i1);
@@ -1056,62 +1128,47 @@ struct MergeArgs {
   const float* lse_part;
   void* o;
   float* lse_out;
+  int64_t rows;
   int32_t n_split, o_f32;
 };
 
+// One wave per (sequence, query, head) row: lanes over splits for the max and
+// the normaliser, lanes over dimensions for the weighted sum of the partials.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
-  constexpr int NQ = D / 4;       // threads per split (4 dims each)
-  constexpr int NSG = 256 / NQ;   // splits handled in parallel
-  __shared__ float red[4];
-  __shared__ f32x4 accs[256];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t row = blockIdx.x;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
   const float* lp = a.lse_part + row * a.n_split;
   const float* op = a.o_part + row * a.n_split * D;
-
   float mx = -INFINITY;
-  for (int i = tid; i < a.n_split; i += 256) mx = fmaxf(mx, lp[i]);
+  for (int i = lane; i < a.n_split; i += 64) mx = fmaxf(mx, lp[i]);
   mx = wave_max(mx);
-  if (lane == 0) red[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  const bool empty = M == -INFINITY;
+  const bool empty = mx == -INFINITY;
   float z = 0.0f;
   if (!empty)
-    for (int i = tid; i < a.n_split; i += 256) z += expf(lp[i] - M);
+    for (int i = lane; i < a.n_split; i += 64) z += expf(lp[i] - mx);
   z = wave_sum(z);
-  if (lane == 0) red[w] = z;
-  __syncthreads();
-  const float Z = red[0] + red[1] + red[2] + red[3];
-
-  const int sg = tid / NQ, dq = tid % NQ;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (!empty) {
-    for (int i = sg; i < a.n_split; i += NSG) {
-      const float wgt = expf(lp[i] - M);
-      if (wgt > 0.0f) acc += wgt * *(const f32x4*)(op + (int64_t)i * D + 4 * dq);
-    }
-  }
-  accs[tid] = acc;
-  __syncthreads();
-  if (sg == 0) {
-    f32x4 sum = accs[dq];
+  float acc[E];
 #pragma unroll
-    for (int k = 1; k < NSG; ++k) sum += accs[k * NQ + dq];
-    const float inv = empty ? 0.0f : 1.0f / Z;
-    sum *= inv;
-    if (a.o_f32) {
-      *(f32x4*)((float*)a.o + row * D + 4 * dq) = sum;
-    } else {
-      uint2 v2;
-      v2.x = pack_bf16(sum[0], sum[1]);
-      v2.y = pack_bf16(sum[2], sum[3]);
-      *(uint2*)((uint16_t*)a.o + row * D + 4 * dq) = v2;
+  for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+  if (!empty) {
+#pragma unroll 4
+    for (int i = 0; i < a.n_split; ++i) {
+      const float wgt = expf(lp[i] - mx);
+#pragma unroll
+      for (int j = 0; j < E; ++j) acc[j] = fmaf(wgt, op[(int64_t)i * D + lane + 64 * j], acc[j]);
     }
-    if (dq == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : M + logf(Z);
   }
+  const float inv = empty ? 0.0f : 1.0f / z;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const float v = acc[j] * inv;
+    if (a.o_f32) ((float*)a.o)[row * D + lane + 64 * j] = v;
+    else ((uint16_t*)a.o)[row * D + lane + 64 * j] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  }
+  if (lane == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(z);
 }
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
@@ -1259,8 +1316,8 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     a.scale = d.scale;
     a.c2 = d.scale_log2;
     const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
-    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_narrow_kernel<64>), grid, dim3(256), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_narrow_kernel<64, false>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -1300,6 +1357,43 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
   return check_launch();
 }
 
+int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
+                       const void* q, const void* k_new, const void* v_new, int64_t n_query,
+                       float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
+                       void* stream) {
+  NarrowArgs a{};
+  a.k = (const uint16_t*)kc;
+  a.v = (const uint16_t*)vc;
+  a.q = (const uint16_t*)q;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.rows = d.rows;
+  a.L = d.L;
+  a.blk = d.blk;
+  a.kv_len = kv_len;
+  a.n_query = n_query;
+  a.blk_len = p.blk_len;
+  a.tail_len = p.tail_len;
+  a.per_block = p.per_block;
+  a.n_split = p.n_split;
+  a.n_blocks = d.n_blocks;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.NG = d.B * d.Hkv;
+  a.scale = d.scale;
+  a.c2 = d.scale_log2;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
+  hipStream_t st = (hipStream_t)stream;
+  if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_narrow_kernel<64, true>), grid, dim3(256), 0, st, a);
+  const int rc = check_launch();
+  if (rc) return rc;
+  return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
+}
+
 int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const float* o_part,
                      const float* lse_part, void* o, int32_t o_dtype, float* lse_out,
                      void* stream) {
@@ -1308,9 +1402,10 @@ int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const floa
   a.lse_part = lse_part;
   a.o = o;
   a.lse_out = lse_out;
+  a.rows = (int64_t)d.B * n_query * d.Hq;
   a.n_split = n_split;
   a.o_f32 = o_dtype == STAR_F32;
-  const dim3 grid((unsigned)((int64_t)d.B * n_query * d.Hq));
+  const dim3 grid((unsigned)((a.rows + 3) / 4));
   hipStream_t st = (hipStream_t)stream;
   if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, dim3(256), 0, st, a);

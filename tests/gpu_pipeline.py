@@ -104,13 +104,24 @@ class Pipeline:
                          self.k_tail_rows[row], self.v_tail_rows[row], 1)
         return self.attend(w.ctx_len + row + 1, self.q_tail_rows[row], 1)
 
-    def run_tail(self):
+    def decode_step_fused(self, t):
+        """Decode step t through star_attn_decode_step (append + partials + merge)."""
+        w = self.w
+        row = w.n_query + t
+        kv_len = w.ctx_len + row + 1
+        n_split, o_part, lse_part, o, lse = self.workspace(kv_len, 1)
+        sa.star_attn_decode_step(self.desc, self.k_cache, self.v_cache, kv_len,
+                                 self.q_tail_rows[row], self.k_tail_rows[row],
+                                 self.v_tail_rows[row], 1, o_part, lse_part, o, self.dtype, lse)
+        return o, lse
+
+    def run_tail(self, fused=False):
         """Query step then every decode step; returns host arrays [B, T, Hq, d], [B, T, Hq]."""
         w = self.w
         o, lse = self.query_step()
         outs, lses = [to_host_f64(o)], [lse.cpu().numpy().astype(np.float64)]
         for t in range(w.n_decode):
-            o, lse = self.decode_step(t)
+            o, lse = self.decode_step_fused(t) if fused else self.decode_step(t)
             outs.append(to_host_f64(o))
             lses.append(lse.cpu().numpy().astype(np.float64))
         return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1)

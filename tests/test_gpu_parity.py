@@ -236,3 +236,31 @@ def test_binding_rejects_wrong_buffers():
         sa.star_attn_phase1(p.desc, p.k_cache[:10], p.v_cache, p.dev["q_ctx"], p.o_ctx)
     with pytest.raises(sa.StarAttnError):
         sa.star_attn_phase2_plan(p.desc, w.ctx_len, 1)
+
+
+@pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g8_narrow", "peaked", "ragged_empty_split",
+                                  "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks"])
+def test_fused_decode_step(runs, name):
+    """star_attn_decode_step (append + partials + merge) against the oracle's
+    decode loop and against the three separate calls, every step."""
+    p0, _, tail_o, tail_l = _pipeline(runs, name)
+    w = p0.w
+    p = Pipeline(w, inputs=p0.inputs, threads=4)
+    p.write_context()
+    fo, fl = p.run_tail(fused=True)
+    torch.cuda.synchronize()
+    x = {k: _f64(w, v) for k, v in p.inputs.items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    ref_o, ref_l = orc.decode_loop(x["q_tail"], x["k_ctx"], x["v_ctx"], x["k_tail"],
+                                   x["v_tail"], w.n_query, sc)
+    d = slice(w.n_query, None)
+    eo, el = _err(fo[:, d], ref_o[:, d]), _err(fl[:, d], ref_l[:, d])
+    print(f"{name}: fused decode max-abs error o {eo:.3e}, lse {el:.3e}")
+    assert eo <= TOL[w.dtype] and el <= TOL_LSE[w.dtype]
+    # same partial arithmetic as the separate calls: outputs agree to the
+    # output rounding (bf16: one ulp of |o| < 8 is 2^-5 at most)
+    assert _err(fo[:, d], tail_o[:, d]) <= (1e-6 if w.dtype == "f32" else 2 ** -5)
+    assert _err(fl[:, d], tail_l[:, d]) <= 1e-4
+    # the appended rows landed in the cache exactly as star_kv_write puts them
+    assert torch.equal(p.k_cache.view(torch.int16), p0.k_cache.view(torch.int16))
+    assert torch.equal(p.v_cache.view(torch.int16), p0.v_cache.view(torch.int16))
