@@ -8,10 +8,11 @@ autoregressive decode loop (n_decode steps of append + partials + merge).
 Prints ONE JSON line. ``value`` is the phase-1 context throughput (tokens/s)
 measured inside the timed steps; the decode figure (µs per step and per
 token) is reported beside it. ``roofline`` is for the dominant kernel
-(phase 1, MFMA-bound), ``roofline_phase2`` for the decode partial kernel
-(HBM-bound); both are computed from HIP events recorded on the launch stream
-around every launch of that kernel in the timed steps. ``cpu_baseline`` is
-the fp64 oracle timed on a bounded sample on the host.
+(phase 1, MFMA-bound), from HIP events recorded on the launch stream around
+every phase-1 launch in the timed steps; ``roofline_phase2`` is for the
+decode step (HBM-bound), from events around its two launches (append +
+partials, merge). ``cpu_baseline`` is the fp64 oracle timed on a bounded
+sample on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -44,13 +45,17 @@ def phase1_flops(w) -> float:
 
 
 def decode_bytes(w, kv_len: int, n_split: int) -> float:
-    """Algorithmic HBM bytes of one decode partial launch: K+V rows [0, kv_len),
-    the query rows, and the fp32 partials written."""
+    """Algorithmic HBM bytes of one decode step (its two launches): the new
+    token's K/V row written, K+V rows [0, kv_len) and the query read once, the
+    fp32 split partials written and read back by the merge, the output row
+    and its LSE written."""
     elt = 2 if w.dtype == "bf16" else 4
+    append = 2.0 * w.batch * w.n_kv_heads * w.head_dim * elt
     kv = 2.0 * w.batch * w.n_kv_heads * kv_len * w.head_dim * elt
     q = w.batch * w.n_q_heads * w.head_dim * elt
-    parts = w.batch * w.n_q_heads * n_split * (w.head_dim + 1) * 4
-    return kv + q + parts
+    parts = 2.0 * w.batch * w.n_q_heads * n_split * (w.head_dim + 1) * 4
+    out = w.batch * w.n_q_heads * (w.head_dim * elt + 4)
+    return append + kv + q + parts + out
 
 
 def cpu_baseline(w, inputs, budget_s: float = 12.0):
@@ -86,22 +91,38 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
                       f"from sequence 0, all {w.n_q_heads} query heads, {wall:.1f} s wall"}
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 FETCH/WRITE counters, if
-    they were taken on the current kernel source; else None."""
+def load_traffic(*kernels):
+    """HBM bytes per launch, summed over the given kernels, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
+    kernel source; else None."""
     try:
         doc = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    ent = doc.get(kernel)
-    if not ent:
-        return None
-    import hashlib
-    src = os.path.join(ROOT, "long_context_attention_phase1_amd", "csrc", "star_kernels.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if ent.get("source_sha256_16") != h:
-        return None
-    return ent.get("bytes_per_launch")
+    from long_context_attention_phase1_amd.profiling import source_sha
+    sha = source_sha()
+    total = 0.0
+    for k in kernels:
+        ent = doc.get(k)
+        if not ent or ent.get("source_sha256_16") != sha:
+            return None
+        total += ent["bytes_per_launch"]
+    return total
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES (read once, written once): the
+    reference volume that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    from long_context_attention_phase1_amd.profiling import COPY_BYTES
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -112,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="llama8b_128k_peaked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is measured on one GPU's share "
@@ -127,6 +150,8 @@ def main():
 
     w = syn.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
     t_gen = time.perf_counter()
     inputs = syn.make_inputs(w, args.threads)
     p = Pipeline(w, inputs=inputs, fill_nan=False)
@@ -161,6 +186,7 @@ def main():
                 k0 = ev()
                 k0.record(stream)
             # append the token's K/V + split partials (one launch), then the merge
+            # (a second launch); the events bracket both
             sa.star_attn_decode_step(p.desc, p.k_cache, p.v_cache, kv_len, p.q_tail_rows[row],
                                      p.k_tail_rows[row], p.v_tail_rows[row], 1, o_part, lse_part,
                                      o, p.dtype, lse)
@@ -200,9 +226,9 @@ def main():
     dec_gbs = float(np.sum(dec_bytes) / (np.sum(dec_kernel_ms) * 1e-3) / 1e9)
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
-    kname1 = "attn_wide_kernel<128,phase1>"
-    kname2 = "attn_narrow_kernel<128,fused>"
-    t1, t2 = load_traffic(kname1), load_traffic(kname2)
+    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true>"
+    kname2 = (f"attn_narrow_kernel<{w.head_dim}, true>", f"lse_merge_kernel<{w.head_dim}>")
+    t1, t2 = load_traffic(kname1), load_traffic(*kname2)
     out = {
         "metric": METRIC,
         "value": ctx_tok_s,
@@ -226,16 +252,17 @@ def main():
         "query_step_ms": q_ms,
         "decode_us_per_step": step_us,
         "decode_us_per_token": step_us / w.batch,
-        "decode_partial_kernel_us": float(np.mean(dec_kernel_ms) * 1e3),
+        "decode_step_kernels_us": float(np.mean(dec_kernel_ms) * 1e3),
         "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
                      "traffic": t1, "kernel": kname1,
                      "algorithmic": f"{flops:.4e} FLOP per launch (4*d per visible pair)"},
         "roofline_phase2": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS, "traffic": t2,
-                            "kernel": kname2,
-                            "algorithmic": "K+V rows [0, kv_len) + q + fp32 partials per launch "
-                                           "(one fused decode-step launch: append, partials, merge)"},
+                            "kernel": " + ".join(kname2),
+                            "algorithmic": "per decode step: K+V rows [0, kv_len) and q read, "
+                                           "new K/V row written, fp32 partials written and "
+                                           "re-read, output row written"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)

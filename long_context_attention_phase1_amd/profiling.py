@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 CSV output for the committed profile records.
+
+``python -m long_context_attention_phase1_amd.profiling stats DIR OUT.txt -- CMD``
+    formats the kernel_stats.csv of a ``rocprofv3 --kernel-trace --stats
+    --output-format csv`` run (per-kernel calls, total/avg/min/max duration).
+
+``python -m long_context_attention_phase1_amd.profiling traffic FETCH_DIR WRITE_DIR OUT``
+    reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
+    ``bench.py --copy-calibration`` and writes, per kernel and launch shape,
+    the HBM bytes per launch. Both counters are in KiB per dispatch; each is
+    scaled by what it reads on the plain device-to-device copy of known size
+    that the calibration run performs first (``COPY_BYTES`` read and written
+    once), so the figures are in the same units as the algorithmic bytes.
+
+Host-only text processing; no GPU work.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+COPY_BYTES = 1 << 30
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(PKG, "csrc", "star_kernels.hip")
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    """Demangled kernel name without namespaces and argument lists."""
+    n = name.replace("star::(anonymous namespace)::", "")
+    n = re.sub(r"\((?:[^()]|\([^()]*\))*\)\s*$", "", n).strip()
+    if n.startswith("void "):
+        n = n[5:]
+    return n
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def stats(d: str, out: str, command: str) -> None:
+    rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}",
+             f"# kernel source sha256[:16]: {source_sha()}",
+             f"{'kernel':58s} {'calls':>6s} {'total ms':>10s} {'avg us':>10s} "
+             f"{'min us':>10s} {'max us':>10s} {'%':>6s}"]
+    for r in rows:
+        lines.append(f"{short_name(r['Name'])[:58]:58s} {int(r['Calls']):6d} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
+                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _dispatches(d: str, counter: str):
+    """{dispatch id: (kernel short name, grid size, counter value in KiB)}."""
+    out = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            out[int(r["Dispatch_Id"])] = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]),
+                                          float(r["Counter_Value"]))
+    return out
+
+
+def _calibration(disp, counter: str) -> float:
+    """Scale that turns the counter into bytes: COPY_BYTES over its mean value
+    on the device-to-device copies of COPY_BYTES (runtime blit kernel) that the
+    calibration run issues."""
+    vals = [v for k, _, v in disp.values() if k == "__amd_rocclr_copyBuffer"]
+    if counter == "WRITE_SIZE":
+        vals = [v for v in vals if abs(v * 1024 - COPY_BYTES) < 0.01 * COPY_BYTES]
+    vals = [v for v in vals if v * 1024 > COPY_BYTES / 8]
+    if not vals:
+        raise RuntimeError("calibration copy not found in the counter run")
+    return COPY_BYTES / (sum(vals) / len(vals) * 1024)
+
+
+def traffic(fetch_dir: str, write_dir: str, out_json: str, out_txt: str, commands) -> None:
+    fetch = _dispatches(fetch_dir, "FETCH_SIZE")
+    write = _dispatches(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = _calibration(fetch, "FETCH_SIZE"), _calibration(write, "WRITE_SIZE")
+    # library kernels only, grouped by (kernel, grid): one group per launch shape
+    groups = defaultdict(list)
+    for i, (k, grid, fv) in fetch.items():
+        if i in write and write[i][0] == k and "_kernel<" in k and not k.startswith("at::"):
+            groups[(k, grid)].append((fv, write[i][2]))
+    sha = source_sha()
+    doc = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_scale": f_scale,
+                            "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer",
+                            "commands": list(commands)}}
+    lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch)",
+             *[f"# command: {c}" for c in commands],
+             f"# calibration: device-to-device copy of {COPY_BYTES} B (runtime blit kernel) -> "
+             f"bytes = FETCH_SIZE KiB x 1024 x {f_scale:.4f} + WRITE_SIZE KiB x 1024 x "
+             f"{w_scale:.4f}",
+             f"# kernel source sha256[:16]: {sha}",
+             f"{'kernel':40s} {'grid':>9s} {'disp':>5s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} "
+             f"{'bytes/launch':>13s}"]
+    best = {}
+    for (k, grid), vals in sorted(groups.items()):
+        fv = sum(v[0] for v in vals) / len(vals)
+        wv = sum(v[1] for v in vals) / len(vals)
+        b = fv * 1024 * f_scale + wv * 1024 * w_scale
+        lines.append(f"{k[:40]:40s} {grid:9d} {len(vals):5d} {fv:12.1f} {wv:12.1f} {b:13.4e}")
+        # per kernel: the launch shape issued most often (the decode loop's)
+        if k not in best or len(vals) > best[k]["dispatches"]:
+            best[k] = {"grid": grid, "dispatches": len(vals), "fetch_kib": fv, "write_kib": wv,
+                       "bytes_per_launch": b, "source_sha256_16": sha}
+    doc.update(best)
+    json.dump(doc, open(out_json, "w"), indent=1)
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _main(argv):
+    if argv[:1] == ["stats"] and "--" in argv:
+        i = argv.index("--")
+        stats(argv[1], argv[2], " ".join(argv[i + 1:]))
+    elif argv[:1] == ["traffic"] and "--" in argv:
+        i = argv.index("--")
+        cmds = " ".join(argv[i + 1:]).split(" ;; ")
+        traffic(argv[1], argv[2], argv[3], argv[4], cmds)
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(_main(sys.argv[1:]))
