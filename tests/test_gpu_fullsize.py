@@ -1,0 +1,102 @@
+"""GPU parity at the full sizes of the four bf16 workloads of the scope table.
+
+Each workload runs on the GPU exactly as bench.py times it: context
+kv_write, phase 1, the query step (kv_write + partials + merge), then every
+decode step through star_attn_decode_step. The fp64 oracle then recomputes
+a sample of outputs one by one:
+  * phase 1: rows at the edges of the first, second, a middle and the last
+    block (first rows, tile boundaries, mid-block, last row) plus random
+    rows, every query head, each sequence;
+  * phase 2: the first, middle and last query rows and the first and last
+    decode steps, every head, output and log-sum-exp.
+Every output is also checked for the property that holds at any size: it is
+finite and, being a convex combination of V rows, no larger in magnitude than
+the largest |V| element.
+
+Tolerances as for the small workloads: max-abs 2e-2 on bf16 outputs, 2e-3 on
+the fp32 log-sum-exp.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_phase1_amd import synthetic as syn
+from oracle import star_oracle as orc
+from tests.gpu_pipeline import Pipeline, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 2e-2, 2e-3
+FULL = ["llama8b_32k", "llama8b_128k_peaked", "llama8b_1m", "llama70b_256k_b4"]
+
+
+def _ctx_rows(w, rng, n_random=4):
+    """Sampled context rows: edges of blocks 0, 1, n/2, n-1, plus random rows."""
+    rows = set()
+    for i in sorted({0, 1, w.n_blocks // 2, w.n_blocks - 1}):
+        lo, hi = i * w.block_len, min((i + 1) * w.block_len, w.ctx_len)
+        for r in (lo, lo + 1, lo + 63, lo + 64, lo + (hi - lo) // 2, hi - 1):
+            if lo <= r < hi:
+                rows.add(r)
+    rows.update(int(x) for x in rng.integers(0, w.ctx_len, size=n_random))
+    return sorted(rows)
+
+
+def _tail_rows(w):
+    return sorted({0, w.n_query // 2, w.n_query - 1, w.n_query, w.n_query + w.n_decode - 1})
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+    w = syn.WORKLOADS[name]
+    threads = min(16, os.cpu_count() or 1)
+    p = Pipeline(w, threads=threads, fill_nan=False)
+    p.write_context()
+    p.phase1()
+    tail_o, tail_l = p.run_tail(fused=True)
+    torch.cuda.synchronize()
+
+    # property over every output: finite and bounded by max |V|
+    vmax = max(float(p.dev["v_ctx"].abs().max()), float(p.dev["v_tail"].abs().max()))
+    assert bool(torch.isfinite(p.o_ctx).all())
+    assert float(p.o_ctx.abs().max()) <= vmax * (1 + 2 ** -7)
+    assert np.isfinite(tail_o).all() and np.isfinite(tail_l).all()
+    assert np.abs(tail_o).max() <= vmax * (1 + 2 ** -7)
+
+    x = p.inputs
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    G = w.group
+    rng = np.random.default_rng(123)
+    rows = _ctx_rows(w, rng)
+    trows = _tail_rows(w)
+    max_row = max(rows) + 1
+    e1 = e2 = el = 0.0
+    for s in range(w.batch):
+        o_gpu = to_host_f64(p.o_ctx[s, rows])                       # [n, Hq, d]
+        q_rows = syn.to_f64(x["q_ctx"][s, rows], w.dtype)           # [n, Hq, d]
+        qt = syn.to_f64(x["q_tail"][s, trows], w.dtype)
+        pos = [w.ctx_len + t for t in trows]
+        for g in range(w.n_kv_heads):
+            hs = slice(g * G, (g + 1) * G)
+            K = syn.to_f64(x["k_ctx"][s, :, g], w.dtype)
+            V = syn.to_f64(x["v_ctx"][s, :, g], w.dtype)
+            ref1 = orc.phase1_rows_one_head(q_rows[:, hs], K[:max_row], V[:max_row], rows,
+                                            w.block_len, w.anchor_len, sc)
+            e1 = max(e1, float(np.abs(o_gpu[:, hs] - ref1).max()))
+            Ka = np.concatenate([K, syn.to_f64(x["k_tail"][s, :, g], w.dtype)])
+            Va = np.concatenate([V, syn.to_f64(x["v_tail"][s, :, g], w.dtype)])
+            del K, V
+            ref_o, ref_l = orc.phase2_rows_one_head(qt[:, hs], Ka, Va, pos, sc)
+            e2 = max(e2, float(np.abs(tail_o[s, trows][:, hs] - ref_o).max()))
+            el = max(el, float(np.abs(tail_l[s, trows][:, hs] - ref_l).max()))
+            del Ka, Va
+    print(f"{name}: {len(rows)} ctx rows x {w.batch} seqs, {len(trows)} tail rows; "
+          f"max-abs phase 1 {e1:.3e}, phase 2 o {e2:.3e}, lse {el:.3e}")
+    assert e1 <= TOL_O
+    assert e2 <= TOL_O
+    assert el <= TOL_LSE
