@@ -58,12 +58,48 @@ int validate_phase2(const Dims& d, int64_t kv_len, int64_t n_query) {
   return STAR_OK;
 }
 
+static int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Balanced decode plan (see Plan): equal tile-aligned ranges, at most one
+// host boundary inside each. Returns false when the shape does not allow it.
+static bool balanced_plan(const Dims& d, int64_t kv_len, Plan* p) {
+  if (d.dtype != STAR_BF16 || d.blk % kTile != 0 || d.L % kTile != 0) return false;
+  const int64_t groups = (int64_t)d.B * d.Hkv;
+  int64_t w = kNarrowWorkgroups / groups;
+  if (w < 1) w = 1;
+  int64_t r = round_up(cdiv(kv_len, w), kTile);
+  if (r < 512) r = 512;
+  w = cdiv(kv_len, r);
+  int64_t n_split = 0;
+  for (int64_t j = 0; j < w; ++j) {
+    const int64_t a = j * r, b = a + r < kv_len ? a + r : kv_len;
+    const int64_t bnd = inner_boundary(d.L, d.blk, d.n_blocks, a, b);
+    if (bnd >= 0 && inner_boundary(d.L, d.blk, d.n_blocks, bnd, b) >= 0) return false;
+    n_split += bnd >= 0 ? 2 : 1;
+  }
+  if (n_split > (1 << 20)) return false;
+  p->balanced = 1;
+  p->n_wg = (int32_t)w;
+  p->wg_rows = r;
+  p->bnd_period = r / gcd64(d.blk, r);
+  p->n_split = (int32_t)n_split;
+  return true;
+}
+
 Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
   Plan p{};
   const int64_t cols = n_query * d.G;
   p.narrow = (d.dtype != STAR_BF16) || cols <= kNarrowCols;
   p.n_groups = p.narrow ? d.B * d.Hkv : d.B * d.Hkv * d.HQ;
   p.n_qtiles = p.narrow ? 1 : (int32_t)cdiv(n_query, (int64_t)kColsPerWave * d.RW);
+  if (p.narrow && balanced_plan(d, kv_len, &p)) return p;
   // decode: ~one long-running workgroup per CU; many query rows: 8 per CU
   const int64_t total = p.narrow ? kNarrowWorkgroups : kTargetWorkgroups;
   const int64_t min_len = p.narrow ? 512 : 256;

@@ -29,6 +29,17 @@ struct Dims {
 };
 
 // Phase-2 split plan: every split lies inside one host's share.
+//
+// Blockwise plan: each context block is cut into per_block splits of
+// blk_len rows and the tail into tail_splits of tail_len rows; one workgroup
+// per split.
+//
+// Balanced plan (decode kernel, bf16, tile-aligned blocks): the rows
+// [0, kv_len) of every (sequence, kv head) are cut into n_wg equal ranges of
+// wg_rows rows (a multiple of the tile), one workgroup each, so that the
+// whole grid is resident at once. A range holds at most one host boundary
+// (a block start, or the context/tail edge); a range that holds one yields
+// two splits, one on each side. Splits are numbered in row order.
 struct Plan {
   int32_t narrow;         // 1: single-column-tile decode kernel, 0: wide kernel
   int32_t per_block;      // splits per context block
@@ -38,6 +49,10 @@ struct Plan {
   int32_t n_split;
   int32_t n_groups;       // workgroup groups (sequence, kv head[, head sub-group])
   int32_t n_qtiles;       // query-row tiles (wide kernel)
+  int32_t balanced;       // 1: balanced plan
+  int32_t n_wg;           // balanced: workgroups (ranges) per group
+  int64_t wg_rows;        // balanced: rows per range
+  int64_t bnd_period;     // balanced: block starts i*blk with i % bnd_period == 0 fall on a range edge
 };
 
 int validate_desc(const star_attn_desc* d, Dims* out);
@@ -49,6 +64,32 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query);
 #else
 #define STAR_HD
 #endif
+
+// First host boundary strictly inside (lo, hi), or -1. Host boundaries are
+// the block starts i*blk (1 <= i < n_blocks) and the tail start L.
+STAR_HD static inline int64_t inner_boundary(int64_t L, int64_t blk, int32_t n_blocks, int64_t lo,
+                                             int64_t hi) {
+  const int64_t i = lo / blk + 1;
+  if (i <= (int64_t)n_blocks - 1 && i * blk < hi) return i * blk;
+  if (L > lo && L < hi) return L;
+  return -1;
+}
+
+// Balanced plan: number of host boundaries below x that do not fall on a
+// range edge (each adds one split before x).
+STAR_HD static inline int64_t inner_boundaries_below(int64_t L, int64_t blk, int32_t n_blocks,
+                                                     int64_t wg_rows, int64_t bnd_period,
+                                                     int64_t x) {
+  if (x <= 0) return 0;
+  int64_t m = (x - 1) / blk;
+  if (m > (int64_t)n_blocks - 1) m = (int64_t)n_blocks - 1;
+  int64_t c = m - m / bnd_period;
+  if (L < x && L % wg_rows != 0) ++c;
+  return c;
+}
+int validate_desc(const star_attn_desc* d, Dims* out);
+int validate_phase2(const Dims& d, int64_t kv_len, int64_t n_query);
+Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query);
 
 // Split sigma of a plan -> rows [lo, hi) (lo == hi: empty) and host id
 // (context block index, or n_blocks for the tail).
@@ -74,8 +115,29 @@ STAR_HD static inline void split_rows(int64_t L, int64_t blk, int32_t n_blocks, 
 
 static inline void split_range(const Dims& d, const Plan& p, int64_t kv_len, int32_t sigma,
                                int64_t* lo, int64_t* hi, int32_t* host) {
-  split_rows(d.L, d.blk, d.n_blocks, p.per_block, p.blk_len, p.tail_len, kv_len, sigma, lo, hi,
-             host);
+  if (!p.balanced) {
+    split_rows(d.L, d.blk, d.n_blocks, p.per_block, p.blk_len, p.tail_len, kv_len, sigma, lo, hi,
+               host);
+    return;
+  }
+  // balanced plan: walk the ranges in row order, one or two splits each
+  int64_t base = 0;
+  for (int64_t j = 0; j < p.n_wg; ++j) {
+    const int64_t a = j * p.wg_rows;
+    const int64_t b = a + p.wg_rows < kv_len ? a + p.wg_rows : kv_len;
+    const int64_t bnd = inner_boundary(d.L, d.blk, d.n_blocks, a, b);
+    const int64_t n = bnd >= 0 ? 2 : 1;
+    if (sigma < base + n) {
+      const bool second = sigma == base + 1;
+      *lo = second ? bnd : a;
+      *hi = (bnd >= 0 && !second) ? bnd : b;
+      *host = *lo < d.L ? (int32_t)(*lo / d.blk) : d.n_blocks;
+      return;
+    }
+    base += n;
+  }
+  *lo = *hi = kv_len;
+  *host = d.n_blocks;
 }
 
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.

@@ -779,6 +779,9 @@ struct NarrowArgs {
   // decode step (FUSED kernels only): rows appended at kv_len - n_query
   const uint16_t* k_new;  // [B][n_query][Hkv][D]
   const uint16_t* v_new;
+  // balanced plan (see Plan in star_internal.hpp)
+  int64_t wg_rows, bnd_period;
+  int32_t balanced, n_wg;
 };
 
 // One decode iteration: wait for the pair of tiles in stages (2*PI, 2*PI+1),
@@ -834,15 +837,29 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const int tp = w >> 1, kt = w & 1;  // tile of the pair, 32-key slice of the tile
 
-  // splits in reverse order: the short, partly masked tail splits start first
-  // instead of waiting for a CU after the long context splits
+  // work items in reverse order: the range or split holding the tail (with
+  // its masked edge tiles and the appended rows) starts first instead of
+  // waiting for a CU after the long context ranges
   const int gidx = (int)(blockIdx.x % a.NG);
-  const int32_t sigma = a.n_split - 1 - (int32_t)(blockIdx.x / a.NG);
+  const int32_t jj = (int32_t)(blockIdx.x / a.NG);
   const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
-  int64_t lo, hi;
-  int32_t host;
-  split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo, &hi,
-             &host);
+  // rows [lo, hi) of this workgroup; split sigma, and with the balanced plan a
+  // second split sigma + 1 from the host boundary bnd on (bnd = -1: none)
+  int64_t lo, hi, bnd = -1;
+  int32_t sigma;
+  if (a.balanced) {
+    const int64_t j = (int64_t)a.n_wg - 1 - jj;
+    lo = j * a.wg_rows;
+    hi = lo + a.wg_rows < a.kv_len ? lo + a.wg_rows : a.kv_len;
+    bnd = inner_boundary(a.L, a.blk, a.n_blocks, lo, hi);
+    sigma = (int32_t)(j + inner_boundaries_below(a.L, a.blk, a.n_blocks, a.wg_rows, a.bnd_period,
+                                                 lo));
+  } else {
+    sigma = a.n_split - 1 - jj;
+    int32_t host;
+    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo,
+               &hi, &host);
+  }
   const int64_t pos0 = a.kv_len - a.n_query;
   const int ncols = (int)(a.n_query * a.G);
   // column l32 -> (query j, head)
@@ -882,6 +899,22 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[0][dt] = f32x16{};
   float m[1] = {kMinit}, l[1] = {0.0f};
+  // state of the split before bnd, set aside when this wave reaches bnd
+  f32x16 oprev[1][DT];
+  float mprev = kMinit, lprev = 0.0f;
+  bool switched = false;
+  auto switch_split = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      oprev[0][dt] = oacc[0][dt];
+      oacc[0][dt] = f32x16{};
+    }
+    mprev = m[0];
+    lprev = l[0];
+    m[0] = kMinit;
+    l[0] = 0.0f;
+    switched = true;
+  };
 
   u32x4 qop[1][KS];
   auto load_q = [&](u32x4 (&q)[1][KS]) {
@@ -930,11 +963,15 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     // compiler then knows the query registers are complete and inserts no
     // wait inside the loop
     wait_vmcnt<0>();
+    // interior tile (relative to i0) where the second split starts
+    const int tb = bnd >= 0 ? (int)(bnd / 64 - i0) : 0x7fffffff;
     for (int it = 0; it < n_it; it += 2) {
+      if (2 * it + tp >= tb && !switched) switch_split();
       narrow_iteration<D, 0>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + tp < n_int,
                              Kc + STAR_TOFF(2 * it + 4), Vc + STAR_TOFF(2 * it + 4),
                              Kc + STAR_TOFF(2 * it + 5), Vc + STAR_TOFF(2 * it + 5), w);
       if (it + 1 >= n_it) break;
+      if (2 * it + 2 + tp >= tb && !switched) switch_split();
       narrow_iteration<D, 1>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + 2 + tp < n_int,
                              Kc + STAR_TOFF(2 * it + 6), Vc + STAR_TOFF(2 * it + 6),
                              Kc + STAR_TOFF(2 * it + 7), Vc + STAR_TOFF(2 * it + 7), w);
@@ -945,6 +982,9 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   }
 
   if (n_int == 0) load_q(qop);
+  // edge tiles all lie after bnd (bnd is tile-aligned and precedes every
+  // query position), so they belong to the second split
+  if (bnd >= 0 && !switched) switch_split();
 
   // edge tiles (the causal tail, unaligned ends): waves 0,1, masked
   const int n_edge = (int)(i0 - bf) + (int)(bl - i1);
@@ -984,36 +1024,45 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   }
 
   // ---- merge the four waves' (m, l, O) and write the split's partial
-  const float lw = pair_sum(l[0]);
-  if (g == 0) {
-    msm[w][l32] = m[0];
-    lsm[w][l32] = lw;
-  }
   float* osm = (float*)smem;  // [4][32][D]
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oacc[0][dt][i];
-  __syncthreads();
-  for (int idx = tid; idx < 32 * D; idx += 256) {
-    const int c = idx / D, e = idx % D;
-    if (c >= ncols) continue;
-    float M = msm[0][c];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, msm[ww][c]);
-    float Ls = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2((msm[ww][c] - M) * c2);
-      Ls += f * lsm[ww][c];
-      O += f * osm[(ww * 32 + c) * D + e];
+  auto write_split = [&](int32_t sg, const f32x16 (&oa)[1][DT], float mw, float lw_) {
+    const float lw = pair_sum(lw_);
+    if (g == 0) {
+      msm[w][l32] = mw;
+      lsm[w][l32] = lw;
     }
-    const int j = c / a.G, h = kvh * a.G + c % a.G;
-    const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sigma;
-    const bool any = Ls > 0.0f;
-    a.o_part[base * D + e] = any ? O / Ls : 0.0f;
-    if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oa[0][dt][i];
+    __syncthreads();
+    for (int idx = tid; idx < 32 * D; idx += 256) {
+      const int c = idx / D, e = idx % D;
+      if (c >= ncols) continue;
+      float M = msm[0][c];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, msm[ww][c]);
+      float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = fast_exp2((msm[ww][c] - M) * c2);
+        Ls += f * lsm[ww][c];
+        O += f * osm[(ww * 32 + c) * D + e];
+      }
+      const int j = c / a.G, h = kvh * a.G + c % a.G;
+      const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sg;
+      const bool any = Ls > 0.0f;
+      a.o_part[base * D + e] = any ? O / Ls : 0.0f;
+      if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
+    }
+  };
+  if (bnd >= 0) {
+    write_split(sigma, oprev, mprev, lprev);
+    __syncthreads();  // the LDS merge area is reused
+    write_split(sigma + 1, oacc, m[0], l[0]);
+  } else {
+    write_split(sigma, oacc, m[0], l[0]);
   }
 }
 
@@ -1315,7 +1364,11 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     a.NG = d.B * d.Hkv;
     a.scale = d.scale;
     a.c2 = d.scale_log2;
-    const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
+    a.balanced = p.balanced;
+    a.n_wg = p.n_wg;
+    a.wg_rows = p.wg_rows;
+    a.bnd_period = p.bnd_period;
+    const dim3 grid((unsigned)((int64_t)a.NG * (p.balanced ? p.n_wg : p.n_split)));
     if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, false>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_narrow_kernel<64, false>), grid, dim3(256), 0, st, a);
     return check_launch();
@@ -1385,7 +1438,11 @@ int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t
   a.c2 = d.scale_log2;
   a.k_new = (const uint16_t*)k_new;
   a.v_new = (const uint16_t*)v_new;
-  const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
+  a.balanced = p.balanced;
+  a.n_wg = p.n_wg;
+  a.wg_rows = p.wg_rows;
+  a.bnd_period = p.bnd_period;
+  const dim3 grid((unsigned)((int64_t)a.NG * (p.balanced ? p.n_wg : p.n_split)));
   hipStream_t st = (hipStream_t)stream;
   if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, true>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((attn_narrow_kernel<64, true>), grid, dim3(256), 0, st, a);
