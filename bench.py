@@ -10,8 +10,8 @@ measured inside the timed steps; the decode figure (µs per step and per
 token) is reported beside it. ``roofline`` is for the dominant kernel
 (phase 1, MFMA-bound), from HIP events recorded on the launch stream around
 every phase-1 launch in the timed steps; ``roofline_phase2`` is for the
-decode step (HBM-bound), from events around its two launches (append +
-partials, merge). ``cpu_baseline`` is the fp64 oracle timed on a bounded
+decode step (HBM-bound), from events around the whole decode loop (every
+step's two launches: append + partials, merge) divided by the steps. ``cpu_baseline`` is the fp64 oracle timed on a bounded
 sample on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -160,7 +160,7 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    p1_events, dec_events, dec_bytes, q_events = [], [], [], []
+    p1_events, dec_bytes, q_events = [], [], []
 
     def step(record: bool):
         p.write_context()
@@ -182,18 +182,12 @@ def main():
             row = w.n_query + t
             kv_len = w.ctx_len + row + 1
             n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
-            if record:
-                k0 = ev()
-                k0.record(stream)
-            # append the token's K/V + split partials (one launch), then the merge
-            # (a second launch); the events bracket both
+            # append the token's K/V + split partials (one launch), then the
+            # merge (a second launch)
             sa.star_attn_decode_step(p.desc, p.k_cache, p.v_cache, kv_len, p.q_tail_rows[row],
                                      p.k_tail_rows[row], p.v_tail_rows[row], 1, o_part, lse_part,
                                      o, p.dtype, lse)
             if record:
-                k1 = ev()
-                k1.record(stream)
-                dec_events.append((k0, k1))
                 dec_bytes.append(decode_bytes(w, kv_len, n_split))
         d1 = ev()
         d1.record(stream)
@@ -218,12 +212,12 @@ def main():
     p1_ms = float(np.median([a.elapsed_time(b) for a, b in p1_events]))
     p1_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in p1_events]))
     q_ms = float(np.median([a.elapsed_time(b) for a, b in q_events]))
-    dec_loop_ms = float(np.median([a.elapsed_time(b) for a, b in dec_loops]))
-    dec_kernel_ms = np.array([a.elapsed_time(b) for a, b in dec_events])
+    loop_ms = np.array([a.elapsed_time(b) for a, b in dec_loops])
+    dec_loop_ms = float(np.median(loop_ms))
     ctx_tok_s = w.batch * w.ctx_len / (p1_ms * 1e-3)
     flops = phase1_flops(w)
     p1_tflops = flops / (p1_avg_ms * 1e-3) / 1e12
-    dec_gbs = float(np.sum(dec_bytes) / (np.sum(dec_kernel_ms) * 1e-3) / 1e9)
+    dec_gbs = float(np.sum(dec_bytes) / (np.sum(loop_ms) * 1e-3) / 1e9)
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
     kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true>"
@@ -252,7 +246,6 @@ def main():
         "query_step_ms": q_ms,
         "decode_us_per_step": step_us,
         "decode_us_per_token": step_us / w.batch,
-        "decode_step_kernels_us": float(np.mean(dec_kernel_ms) * 1e3),
         "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
                      "traffic": t1, "kernel": kname1,

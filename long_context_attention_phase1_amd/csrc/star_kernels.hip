@@ -795,6 +795,7 @@ __device__ __forceinline__ void narrow_iteration(
   using Gm = Geo<D, 4>;
   wait_vmcnt<2 * Gm::PER>();
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // no LDS read moves above the wait
   // branch-free: a wave without a tile this iteration (odd tile count) reads
   // the clamped duplicate tile and masks every score, leaving its state as is
   f32x16 sc[1];
@@ -832,8 +833,10 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   constexpr int KS = Gm::KS, DT = Gm::DT;
   static_assert(Gm::RING >= 4 * 32 * D * 4, "merge area must fit in the ring");
   __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
+  __shared__ __attribute__((aligned(1024))) char qsm[32 * D * 2];  // query tile [col][D]
   __shared__ float msm[4][32], lsm[4][32];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform: keep it (and what derives from it) scalar
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int tp = w >> 1, kt = w & 1;  // tile of the pair, 32-key slice of the tile
 
@@ -954,15 +957,35 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     const int jmax = n_int - 1;
 #define STAR_TOFF(j) (base_off + (int64_t)((j) < jmax ? (j) : jmax) * 64 * Gm::RB)
     const int n_it = (n_int + 1) / 2;
+    // the query tile arrives by the same direct-to-LDS loads, ahead of the
+    // four stages: 16-byte chunk u (lane-major over the wave's QI loads) of
+    // column u / CH, d-chunk u % CH, lands at byte 16 u of qsm. A column
+    // past ncols loads column 0 and is zeroed when read.
+    constexpr int QI = 32 * D * 2 / 1024 / 4;  // 1-KB loads per wave
+    const char* qbase = (const char*)(a.q + (int64_t)s * a.n_query * a.Hq * D);
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      const int u = (w * QI + i) * 64 + lane;
+      const int c = u / Gm::CH, k = u % Gm::CH;
+      const int cc = c < ncols ? c : 0;
+      const uint32_t off =
+          (uint32_t)((((cc / a.G) * a.Hq + kvh * a.G + cc % a.G) * D + k * 8) * 2);
+      dma16_lds(qbase, off, qsm + (w * QI + i) * 1024);
+    }
     dma_stage_asm<D, 4, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
     dma_stage_asm<D, 4, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
     dma_stage_asm<D, 4, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
     dma_stage_asm<D, 4, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
-    load_q(qop);
-    // one drain before the loop (query and the first four tiles): the
-    // compiler then knows the query registers are complete and inserts no
-    // wait inside the loop
-    wait_vmcnt<0>();
+    // the query loads are the oldest: wait for them alone, then every wave
+    // reads its B operand from LDS (no register load the compiler would drain)
+    wait_vmcnt<4 * Gm::PER>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 v = lds16(qsm + l32 * (D * 2) + (2 * ks + g) * 16);
+      qop[0][ks] = cvalid ? v : u32x4{0, 0, 0, 0};
+    }
     // interior tile (relative to i0) where the second split starts
     const int tb = bnd >= 0 ? (int)(bnd / 64 - i0) : 0x7fffffff;
     for (int it = 0; it < n_it; it += 2) {
