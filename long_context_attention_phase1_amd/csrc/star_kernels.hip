@@ -784,25 +784,51 @@ struct NarrowArgs {
   int32_t balanced, n_wg;
 };
 
-// One decode iteration: wait for the pair of tiles in stages (2*PI, 2*PI+1),
-// compute this wave's slice, then refill those stages with the pair after next.
-template <int D, int PI>
+// Decode ring: kNarrowStages stages, each one 64-key tile laid out as
+// [K tile | transposed V tile] (LDS layouts as in the wide kernel).
+constexpr int kNarrowStages = 5;
+template <int D>
+struct NarrowRing {
+  using Gm = Geo<D, 4>;
+  static constexpr int SB = Gm::KBYTES + Gm::VBYTES;  // bytes per stage
+  static constexpr int BYTES = kNarrowStages * SB;
+};
+
+// This wave's share of the direct-to-LDS loads of one tile into stage ST.
+template <int D, int ST>
+__device__ __forceinline__ void dma_stage_narrow(char* smem, const char* Kt, const char* Vt,
+                                                 const LaneOffsets<D, 4>& lo, int w) {
+  using Gm = Geo<D, 4>;
+  char* st = smem + ST * NarrowRing<D>::SB;
+#pragma unroll
+  for (int j = 0; j < Gm::KI; ++j) dma16_lds(Kt, lo.kd[j], st + (Gm::KI * w + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < Gm::VI; ++j)
+    dma16_lds(Vt, lo.vd[j], st + Gm::KBYTES + (Gm::VI * w + j) * 1024);
+}
+
+// One decode iteration over the pair of tiles in stages (S0, S1): waves 0,1
+// take the tile in S0, waves 2,3 the one in S1 (a 32-key slice each). Waits
+// until both have landed (the other three stages stay in flight), computes
+// this wave's slice, then refills S0 and S1 with the tiles five ahead.
+template <int D, int S0, int S1>
 __device__ __forceinline__ void narrow_iteration(
     char* smem, const LaneOffsets<D, 4>& lo4, const uint32_t (&kq)[Geo<D, 4>::KS],
     const uint32_t (&vq)[2], const u32x4 (&qop)[1][Geo<D, 4>::KS],
     f32x16 (&oacc)[1][Geo<D, 4>::DT], float (&m)[1], float (&l)[1], float c2, bool active,
-    const char* Ka, const char* Va, const char* Kb, const char* Vb, int w) {
+    int tp, const char* Ka, const char* Va, const char* Kb, const char* Vb, int w) {
   using Gm = Geo<D, 4>;
-  wait_vmcnt<2 * Gm::PER>();
+  constexpr int SB = NarrowRing<D>::SB;
+  wait_vmcnt<(kNarrowStages - 2) * Gm::PER>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");  // no LDS read moves above the wait
+  const uint32_t st = (uint32_t)(tp ? S1 * SB : S0 * SB);
   // branch-free: a wave without a tile this iteration (odd tile count) reads
   // the clamped duplicate tile and masks every score, leaving its state as is
   f32x16 sc[1];
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks)
-    sc[0] = mfma_bf16(lds16(smem + kq[ks] + PI * 2 * Gm::KBYTES), qop[0][ks],
-                      ks == 0 ? f32x16{} : sc[0]);
+    sc[0] = mfma_bf16(lds16(smem + st + kq[ks]), qop[0][ks], ks == 0 ? f32x16{} : sc[0]);
   if (!active) sc[0] = f32x16{} - INFINITY;
   float mx[1];
   slice_max3<1>(sc, mx);
@@ -813,28 +839,31 @@ __device__ __forceinline__ void narrow_iteration(
   for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      oacc[0][dt] = mfma_bf16(lds16(smem + vq[kb] + (PI * 2 * Gm::VBYTES + dt * 32 * 128)),
-                              p[0][kb], oacc[0][dt]);
+      oacc[0][dt] = mfma_bf16(lds16(smem + st + vq[kb] + dt * 32 * 128), p[0][kb], oacc[0][dt]);
   block_sync_lds();
-  dma_stage_asm<D, 4, 2 * PI>(smem, Ka, Va, lo4, w);
-  dma_stage_asm<D, 4, 2 * PI + 1>(smem, Kb, Vb, lo4, w);
+  dma_stage_narrow<D, S0>(smem, Ka, Va, lo4, w);
+  dma_stage_narrow<D, S1>(smem, Kb, Vb, lo4, w);
 }
 
-// Decode partial kernel. One workgroup per (sequence, kv head, split); the
-// split's interior 64-key tiles stream through a ring of four LDS stages by
-// direct-to-LDS loads, two tiles per iteration, the next iteration's two in
+// Decode partial kernel. One workgroup per (sequence, kv head, range or
+// split); its interior 64-key tiles stream through a ring of five LDS stages
+// by direct-to-LDS loads, two tiles per iteration with the next three in
 // flight. Waves 0,1 take the 32-key slices of the even tile, waves 2,3 those
 // of the odd tile, each with its own softmax state; the four states are
-// merged through LDS at the end. Sized so ~one workgroup per CU streams a
-// long contiguous key range with ~128 KB of loads outstanding.
+// merged through LDS at the end. Sized so one workgroup per CU streams a
+// long contiguous key range with 96-160 KB of loads outstanding.
 template <int D, bool FUSED>
 __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   using Gm = Geo<D, 4>;
+  using Ring = NarrowRing<D>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
-  static_assert(Gm::RING >= 4 * 32 * D * 4, "merge area must fit in the ring");
-  __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
-  __shared__ __attribute__((aligned(1024))) char qsm[32 * D * 2];  // query tile [col][D]
-  __shared__ float msm[4][32], lsm[4][32];
+  // after the stream the ring holds the merge area: per split (up to two)
+  // and wave, O as [D][33] (padded: conflict-free both ways), then m and l
+  constexpr int OSM_BYTES = 2 * 4 * D * 33 * 4;
+  static_assert(OSM_BYTES + 2 * 2 * 4 * 32 * 4 <= Ring::BYTES, "merge area must fit in the ring");
+  static_assert(Gm::V_AT + Gm::VBYTES <= Ring::BYTES, "edge tiles must fit in the ring");
+  static_assert(32 * D * 2 <= Ring::SB, "query tile must fit in one stage");
+  __shared__ __attribute__((aligned(1024))) char smem[Ring::BYTES];
   // the wave index is uniform: keep it (and what derives from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -944,24 +973,25 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   if (n_int > 0) {
     LaneOffsets<D, 4> lo4;
     lo4.init(l32, g, w, lane);
-    // this wave's operand offsets: its tile of the pair and its slice
+    // this wave's operand offsets inside a stage: its 32-key slice
     uint32_t kq[KS], vq[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kq[ks] = lo4.kq[ks] + tp * Gm::KBYTES + kt * 32 * Gm::RB;
+    for (int ks = 0; ks < KS; ++ks) kq[ks] = lo4.kq[ks] + kt * 32 * Gm::RB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      vq[kb] = (uint32_t)(Gm::V_AT + tp * Gm::VBYTES) + v_off(l32, 4 * kt + 2 * kb + g);
+      vq[kb] = (uint32_t)Gm::KBYTES + v_off(l32, 4 * kt + 2 * kb + g);
     const char* Kc = (const char*)K;
     const char* Vc = (const char*)V;
     const int64_t base_off = i0 * 64 * (int64_t)Gm::RB;
     const int jmax = n_int - 1;
 #define STAR_TOFF(j) (base_off + (int64_t)((j) < jmax ? (j) : jmax) * 64 * Gm::RB)
     const int n_it = (n_int + 1) / 2;
-    // the query tile arrives by the same direct-to-LDS loads, ahead of the
-    // four stages: 16-byte chunk u (lane-major over the wave's QI loads) of
-    // column u / CH, d-chunk u % CH, lands at byte 16 u of qsm. A column
-    // past ncols loads column 0 and is zeroed when read.
+    // the query tile arrives by the same direct-to-LDS loads, into stage 4
+    // before that stage's first tile: 16-byte chunk u (lane-major over the
+    // wave's QI loads) of column u / CH, d-chunk u % CH, lands at byte 16 u.
+    // A column past ncols loads column 0 and is zeroed when read.
     constexpr int QI = 32 * D * 2 / 1024 / 4;  // 1-KB loads per wave
+    char* qsm = smem + 4 * Ring::SB;
     const char* qbase = (const char*)(a.q + (int64_t)s * a.n_query * a.Hq * D);
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
@@ -972,12 +1002,13 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
           (uint32_t)((((cc / a.G) * a.Hq + kvh * a.G + cc % a.G) * D + k * 8) * 2);
       dma16_lds(qbase, off, qsm + (w * QI + i) * 1024);
     }
-    dma_stage_asm<D, 4, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
-    dma_stage_asm<D, 4, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
-    dma_stage_asm<D, 4, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
-    dma_stage_asm<D, 4, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
+    dma_stage_narrow<D, 0>(smem, Kc + STAR_TOFF(0), Vc + STAR_TOFF(0), lo4, w);
+    dma_stage_narrow<D, 1>(smem, Kc + STAR_TOFF(1), Vc + STAR_TOFF(1), lo4, w);
+    dma_stage_narrow<D, 2>(smem, Kc + STAR_TOFF(2), Vc + STAR_TOFF(2), lo4, w);
+    dma_stage_narrow<D, 3>(smem, Kc + STAR_TOFF(3), Vc + STAR_TOFF(3), lo4, w);
     // the query loads are the oldest: wait for them alone, then every wave
-    // reads its B operand from LDS (no register load the compiler would drain)
+    // reads its B operand from LDS (no register load the compiler would
+    // drain), and stage 4 gets its tile once every wave has read it
     wait_vmcnt<4 * Gm::PER>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -986,19 +1017,31 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
       const u32x4 v = lds16(qsm + l32 * (D * 2) + (2 * ks + g) * 16);
       qop[0][ks] = cvalid ? v : u32x4{0, 0, 0, 0};
     }
+    block_sync_lds();
+    dma_stage_narrow<D, 4>(smem, Kc + STAR_TOFF(4), Vc + STAR_TOFF(4), lo4, w);
     // interior tile (relative to i0) where the second split starts
     const int tb = bnd >= 0 ? (int)(bnd / 64 - i0) : 0x7fffffff;
-    for (int it = 0; it < n_it; it += 2) {
-      if (2 * it + tp >= tb && !switched) switch_split();
-      narrow_iteration<D, 0>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + tp < n_int,
-                             Kc + STAR_TOFF(2 * it + 4), Vc + STAR_TOFF(2 * it + 4),
-                             Kc + STAR_TOFF(2 * it + 5), Vc + STAR_TOFF(2 * it + 5), w);
-      if (it + 1 >= n_it) break;
-      if (2 * it + 2 + tp >= tb && !switched) switch_split();
-      narrow_iteration<D, 1>(smem, lo4, kq, vq, qop, oacc, m, l, c2, 2 * it + 2 + tp < n_int,
-                             Kc + STAR_TOFF(2 * it + 6), Vc + STAR_TOFF(2 * it + 6),
-                             Kc + STAR_TOFF(2 * it + 7), Vc + STAR_TOFF(2 * it + 7), w);
+    // iteration k takes tiles 2k, 2k + 1 from stages (2k) % 5, (2k + 1) % 5
+#define STAR_ITER(S0, S1, K)                                                                  \
+  {                                                                                           \
+    const int t0 = 2 * (K);                                                                   \
+    if (t0 + tp >= tb && !switched) switch_split();                                           \
+    narrow_iteration<D, S0, S1>(smem, lo4, kq, vq, qop, oacc, m, l, c2, t0 + tp < n_int, tp,  \
+                                Kc + STAR_TOFF(t0 + 5), Vc + STAR_TOFF(t0 + 5),               \
+                                Kc + STAR_TOFF(t0 + 6), Vc + STAR_TOFF(t0 + 6), w);           \
+  }
+    for (int k = 0; k < n_it; k += 5) {
+      STAR_ITER(0, 1, k)
+      if (k + 1 >= n_it) break;
+      STAR_ITER(2, 3, k + 1)
+      if (k + 2 >= n_it) break;
+      STAR_ITER(4, 0, k + 2)
+      if (k + 3 >= n_it) break;
+      STAR_ITER(1, 2, k + 3)
+      if (k + 4 >= n_it) break;
+      STAR_ITER(3, 4, k + 4)
     }
+#undef STAR_ITER
 #undef STAR_TOFF
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -1046,46 +1089,54 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     }
   }
 
-  // ---- merge the four waves' (m, l, O) and write the split's partial
-  float* osm = (float*)smem;  // [4][32][D]
-  auto write_split = [&](int32_t sg, const f32x16 (&oa)[1][DT], float mw, float lw_) {
-    const float lw = pair_sum(lw_);
+  // ---- merge the four waves' (m, l, O) of each split and write the partials
+  // (the ring is idle here: every load has landed and every read is done)
+  const int nsp = bnd >= 0 ? 2 : 1;  // slot 0: split sigma, slot 1: sigma + 1
+  float* osm = (float*)smem;                                      // [2][4][D][33]
+  float* msm = (float*)(smem + OSM_BYTES);                        // [2][4][32]
+  float* lsm = msm + 2 * 4 * 32;                                  // [2][4][32]
+  auto stage_state = [&](int sp, const f32x16 (&oa)[1][DT], float mw, float lraw) {
+    const float lw = pair_sum(lraw);
     if (g == 0) {
-      msm[w][l32] = mw;
-      lsm[w][l32] = lw;
+      msm[(sp * 4 + w) * 32 + l32] = mw;
+      lsm[(sp * 4 + w) * 32 + l32] = lw;
     }
+    if (cvalid) {
+      float* ow = osm + (sp * 4 + w) * D * 33 + l32;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        osm[(w * 32 + l32) * D + 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)] = oa[0][dt][i];
-    __syncthreads();
-    for (int idx = tid; idx < 32 * D; idx += 256) {
-      const int c = idx / D, e = idx % D;
-      if (c >= ncols) continue;
-      float M = msm[0][c];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, msm[ww][c]);
-      float Ls = 0.0f, O = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = fast_exp2((msm[ww][c] - M) * c2);
-        Ls += f * lsm[ww][c];
-        O += f * osm[(ww * 32 + c) * D + e];
-      }
-      const int j = c / a.G, h = kvh * a.G + c % a.G;
-      const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sg;
-      const bool any = Ls > 0.0f;
-      a.o_part[base * D + e] = any ? O / Ls : 0.0f;
-      if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
+        for (int i = 0; i < 16; ++i) ow[(32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)) * 33] = oa[0][dt][i];
     }
   };
   if (bnd >= 0) {
-    write_split(sigma, oprev, mprev, lprev);
-    __syncthreads();  // the LDS merge area is reused
-    write_split(sigma + 1, oacc, m[0], l[0]);
+    stage_state(0, oprev, mprev, lprev);
+    stage_state(1, oacc, m[0], l[0]);
   } else {
-    write_split(sigma, oacc, m[0], l[0]);
+    stage_state(0, oacc, m[0], l[0]);
+  }
+  __syncthreads();
+  const int per = ncols * D;
+  for (int idx = tid; idx < nsp * per; idx += 256) {
+    const int sp = idx / per, rem = idx - sp * per;
+    const int c = rem / D, e = rem - c * D;
+    const float* ms = msm + sp * 4 * 32 + c;
+    const float* ls = lsm + sp * 4 * 32 + c;
+    float M = ms[0];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, ms[ww * 32]);
+    float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = fast_exp2((ms[ww * 32] - M) * c2);
+      Ls += f * ls[ww * 32];
+      O += f * osm[((sp * 4 + ww) * D + e) * 33 + c];
+    }
+    const int j = c / a.G, h = kvh * a.G + c % a.G;
+    const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sigma + sp;
+    const bool any = Ls > 0.0f;
+    a.o_part[base * D + e] = any ? O / Ls : 0.0f;
+    if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
   }
 }
 
