@@ -7,7 +7,8 @@
 //                       output) and by phase-2 partials with many query rows
 //   attn_narrow_kernel  split-KV decode partials (<= 32 query columns)
 //   attn_f32_kernel     fp32 path (VALU) for both phases
-//   lse_merge_kernel    exact softmax renormalisation of the partials
+//   lse_merge_kernel    exact softmax renormalisation of the partials (one
+//                       workgroup per output row)
 //
 // Method: Star Attention (hotaipapers.com summary page, podcast transcript,
 // Phase 1 and Phase 2 descriptions; paperhub.cn rebuttal, reply to reviewer
@@ -287,6 +288,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgk0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 __device__ __forceinline__ void block_sync_lds() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
@@ -361,27 +369,13 @@ struct LaneOffsets {
   }
 };
 
-template <int D, int NW, int ST>
-__device__ __forceinline__ void dma_stage(char* smem, const char* Kt, const char* Vt,
-                                          const LaneOffsets<D, NW>& lo, int w) {
-  using Gm = Geo<D, NW>;
-#pragma unroll
-  for (int j = 0; j < Gm::KI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(Kt + lo.kd[j]),
-                                     (lds_void*)(smem + Gm::K_AT + ST * Gm::KBYTES +
-                                                 (Gm::KI * w + j) * 1024), 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < Gm::VI; ++j)
-    __builtin_amdgcn_global_load_lds((const void*)(Vt + lo.vd[j]),
-                                     (lds_void*)(smem + Gm::V_AT + ST * Gm::VBYTES +
-                                                 (Gm::VI * w + j) * 1024), 16, 0, 0);
-}
-
-// The same loads as dma_stage, issued through a minimal asm statement. The
-// compiler then keeps no record of them as LDS writes and inserts no drain of
-// the load counter before the next LDS reads; the caller waits with explicit
-// vmcnt and a barrier before reading a stage (the asm has no register
-// outputs: the data lands in LDS).
+// One direct-to-LDS load (global_load_lds_dwordx4: lane i's 16 bytes from
+// gbase + voff land at LDS lds + 16 i), issued through a minimal asm
+// statement rather than the builtin. The compiler then keeps no record of it
+// as an LDS write and inserts no drain of the load counter before later LDS
+// reads; the caller waits with explicit vmcnt (and lgkmcnt before reusing a
+// stage) and a barrier before reading a stage. The asm has no register
+// outputs: the data lands in LDS.
 //
 // The compiler's hazard recognizer does not look inside asm, so the asm
 // supplies the wait states itself: an SALU write of M0 needs one before an
@@ -523,9 +517,12 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
     for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
   }
   rescale_top<QT, Gm::DT>(mx, m, l, o, c2);
-  wait_vmcnt<Gm::PER>();
+  // tile t + 1 has landed (this wave's loads; the barrier covers the other
+  // waves') and every wave's reads of stage ST + 3 (tile t - 1) are complete
+  wait_vm_lgk0<Gm::PER>();
   __builtin_amdgcn_s_barrier();
-  dma_stage<D, NW, (ST + 3) & 3>(smem, Kt3, Vt3, lo, w);
+  asm volatile("" ::: "memory");  // no LDS read moves above the wait
+  dma_stage_asm<D, NW, (ST + 3) & 3>(smem, Kt3, Vt3, lo, w);
   {
     f32x16 sn[QT];
     u32x4 p[QT][2];
@@ -650,11 +647,12 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     lo.init(l32, g, w, lane);
     const char* Kc = (const char*)K;
     const char* Vc = (const char*)V;
-    dma_stage<D, NW, 0>(smem, Kc + tile_off(0), Vc + tile_off(0), lo, w);
-    dma_stage<D, NW, 1>(smem, Kc + tile_off(1), Vc + tile_off(1), lo, w);
-    dma_stage<D, NW, 2>(smem, Kc + tile_off(2), Vc + tile_off(2), lo, w);
+    dma_stage_asm<D, NW, 0>(smem, Kc + tile_off(0), Vc + tile_off(0), lo, w);
+    dma_stage_asm<D, NW, 1>(smem, Kc + tile_off(1), Vc + tile_off(1), lo, w);
+    dma_stage_asm<D, NW, 2>(smem, Kc + tile_off(2), Vc + tile_off(2), lo, w);
     wait_vmcnt<2 * Gm::PER>();
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the wait
     f32x16 sc[QT];
     float mx[QT];
     qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
@@ -1255,43 +1253,102 @@ struct MergeArgs {
   int32_t n_split, o_f32;
 };
 
-// One wave per (sequence, query, head) row: lanes over splits for the max and
-// the normaliser, lanes over dimensions for the weighted sum of the partials.
+// One workgroup per (sequence, query, head) row. Thread t owns float4
+// column t % (D/4) of the output and the splits i = t / (D/4) (mod SG): all
+// of its partial loads are issued before the log-sum-exp reductions, so the
+// merge costs one round trip to memory; the SG split groups are summed
+// through LDS at the end.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const float* lp = a.lse_part + row * a.n_split;
-  const float* op = a.o_part + row * a.n_split * D;
+  constexpr int C4 = D / 4;       // float4 columns of a row
+  constexpr int SG = 256 / C4;    // split groups
+  constexpr int U = 8;            // splits per thread and batch
+  __shared__ float4 osum[SG][C4];
+  __shared__ float red[4];
+  const int t = threadIdx.x, d4 = t % C4, sg = t / C4, lane = t & 63, wv = t >> 6;
+  const int64_t row = blockIdx.x;
+  const int n = a.n_split;
+  const float* lp = a.lse_part + row * n;
+  const float4* op = (const float4*)(a.o_part + row * (int64_t)n * D);
+  float4 ov[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = sg + SG * u;
+    ov[u] = i < n ? op[(int64_t)i * C4 + d4] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // m = max_s lse_s (block reduction)
   float mx = -INFINITY;
-  for (int i = lane; i < a.n_split; i += 64) mx = fmaxf(mx, lp[i]);
+  for (int i = t; i < n; i += 256) mx = fmaxf(mx, lp[i]);
   mx = wave_max(mx);
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const bool empty = mx == -INFINITY;
+  __syncthreads();
+  // z = sum_s exp(lse_s - m)
   float z = 0.0f;
   if (!empty)
-    for (int i = lane; i < a.n_split; i += 64) z += expf(lp[i] - mx);
+    for (int i = t; i < n; i += 256) z += expf(lp[i] - mx);
   z = wave_sum(z);
-  float acc[E];
-#pragma unroll
-  for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+  if (lane == 0) red[wv] = z;
+  __syncthreads();
+  z = (red[0] + red[1]) + (red[2] + red[3]);
+  // o = sum_s exp(lse_s - m) o_s / z
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (!empty) {
-#pragma unroll 4
-    for (int i = 0; i < a.n_split; ++i) {
-      const float wgt = expf(lp[i] - mx);
 #pragma unroll
-      for (int j = 0; j < E; ++j) acc[j] = fmaf(wgt, op[(int64_t)i * D + lane + 64 * j], acc[j]);
+    for (int u = 0; u < U; ++u) {
+      const int i = sg + SG * u;
+      if (i < n) {
+        const float wgt = expf(lp[i] - mx);
+        acc.x = fmaf(wgt, ov[u].x, acc.x);
+        acc.y = fmaf(wgt, ov[u].y, acc.y);
+        acc.z = fmaf(wgt, ov[u].z, acc.z);
+        acc.w = fmaf(wgt, ov[u].w, acc.w);
+      }
+    }
+    for (int i0 = SG * U; i0 < n; i0 += SG * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + sg + SG * u;
+        ov[u] = i < n ? op[(int64_t)i * C4 + d4] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + sg + SG * u;
+        if (i < n) {
+          const float wgt = expf(lp[i] - mx);
+          acc.x = fmaf(wgt, ov[u].x, acc.x);
+          acc.y = fmaf(wgt, ov[u].y, acc.y);
+          acc.z = fmaf(wgt, ov[u].z, acc.z);
+          acc.w = fmaf(wgt, ov[u].w, acc.w);
+        }
+      }
     }
   }
-  const float inv = empty ? 0.0f : 1.0f / z;
+  osum[sg][d4] = acc;
+  __syncthreads();
+  if (t < C4) {
+    float4 o = osum[0][t];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const float v = acc[j] * inv;
-    if (a.o_f32) ((float*)a.o)[row * D + lane + 64 * j] = v;
-    else ((uint16_t*)a.o)[row * D + lane + 64 * j] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    for (int k = 1; k < SG; ++k) {
+      o.x += osum[k][t].x;
+      o.y += osum[k][t].y;
+      o.z += osum[k][t].z;
+      o.w += osum[k][t].w;
+    }
+    const float inv = empty ? 0.0f : 1.0f / z;
+    const float v[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    if (a.o_f32) {
+      ((float4*)a.o)[row * C4 + t] = float4{v[0], v[1], v[2], v[3]};
+    } else {
+      uint2 b;
+      b.x = pack_bf16(v[0], v[1]);
+      b.y = pack_bf16(v[2], v[3]);
+      ((uint2*)a.o)[row * C4 + t] = b;
+    }
   }
-  if (lane == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(z);
+  if (t == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(z);
 }
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
@@ -1536,7 +1593,7 @@ int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const floa
   a.rows = (int64_t)d.B * n_query * d.Hq;
   a.n_split = n_split;
   a.o_f32 = o_dtype == STAR_F32;
-  const dim3 grid((unsigned)((a.rows + 3) / 4));
+  const dim3 grid((unsigned)a.rows);
   hipStream_t st = (hipStream_t)stream;
   if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, dim3(256), 0, st, a);
