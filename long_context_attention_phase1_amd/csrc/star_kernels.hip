@@ -439,10 +439,12 @@ template <int QT>
 __device__ __forceinline__ void slice_max3(const f32x16 (&s)[QT], float (&mx)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float x = fmaxf(s[qt][0], fmaxf(s[qt][1], s[qt][2]));
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) x = fmaxf(x, fmaxf(s[qt][i], s[qt][i + 1]));
-    x = fmaxf(x, s[qt][15]);
+    // a tree of 3-input maxima (v_max3_f32), depth 3
+    const auto m3 = [](float a, float b, float c) { return fmaxf(fmaxf(a, b), c); };
+    const float x0 = m3(s[qt][0], s[qt][1], s[qt][2]), x1 = m3(s[qt][3], s[qt][4], s[qt][5]);
+    const float x2 = m3(s[qt][6], s[qt][7], s[qt][8]), x3 = m3(s[qt][9], s[qt][10], s[qt][11]);
+    const float x4 = m3(s[qt][12], s[qt][13], s[qt][14]);
+    const float x = fmaxf(m3(x0, x1, x2), m3(x3, x4, s[qt][15]));
     mx[qt] = pair_max(x);
   }
 }
@@ -544,7 +546,8 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   constexpr int WPR = 2 / QT;  // waves per 64-row sub-tile of one head
   static_assert(NW * QT == 8, "workgroup covers 256 columns");
   __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform: keep it (and what derives from it) scalar
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- which (group, work item) this workgroup is
