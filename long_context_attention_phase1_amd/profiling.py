@@ -12,6 +12,12 @@
     that the calibration run performs first (``COPY_BYTES`` read and written
     once), so the figures are in the same units as the algorithmic bytes.
 
+``python -m long_context_attention_phase1_amd.profiling counters OUT.txt DIR... -- CMD``
+    sums the SQ_* / GRBM_GUI_ACTIVE counters of the given ``rocprofv3 --pmc``
+    runs per kernel and derives MFMA utilisation (MFMA-busy cycles over
+    active cycles x SIMDs), LDS utilisation, VALU and co-issue figures and
+    the effective engine clock (active cycles over the kernel duration).
+
 Host-only text processing; no GPU work.
 """
 from __future__ import annotations
@@ -125,10 +131,65 @@ def traffic(fetch_dir: str, write_dir: str, out_json: str, out_txt: str, command
     print("\n".join(lines))
 
 
+SIMDS, CUS, XCDS = 1024, 256, 8
+
+
+def counters(out_txt: str, dirs, command: str, kernels=None) -> None:
+    """Per-kernel counter totals over the given --pmc runs (one dispatch of
+    each kernel of interest per run). A counter taken in several runs (the
+    GRBM_GUI_ACTIVE reference) is averaged over them."""
+    vals = defaultdict(lambda: defaultdict(list))  # kernel -> counter -> per-run totals
+    durs = defaultdict(list)                        # kernel -> per-run dispatch duration (s)
+    for d in dirs:
+        run = defaultdict(lambda: defaultdict(float))
+        spans = {}
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            k = short_name(r["Kernel_Name"])
+            if kernels and k not in kernels:
+                continue
+            run[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            spans[(k, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        for k, c in run.items():
+            for name, v in c.items():
+                vals[k][name].append(v)
+        for (k, _), t in spans.items():
+            durs[k].append(t)
+    lines = ["# rocprofv3 --pmc counters per kernel (summed over the XCDs and shader engines;",
+             "# GRBM_GUI_ACTIVE averaged over the runs that took it)",
+             f"# command: {command}",
+             f"# kernel source sha256[:16]: {source_sha()}"]
+    for k, cl in vals.items():
+        c = {name: sum(v) / len(v) for name, v in cl.items()}
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS  # active cycles of one XCD
+        lines.append(f"{k}")
+        for name in sorted(c):
+            lines.append(f"    {name:32s} {c[name]:.6e}")
+        if gui <= 0:
+            continue
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            lines.append(f"    MFMA busy / (active cycles x SIMDs)        {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * SIMDS):.3f}")
+        if "SQ_LDS_IDX_ACTIVE" in c:
+            lines.append(f"    LDS active / (active cycles x CUs)         {c['SQ_LDS_IDX_ACTIVE'] / (gui * CUS):.3f}")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+            lines.append(f"    MFMA+VALU co-issue / (active x SIMDs)      {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / (gui * SIMDS):.3f}")
+        if "SQ_INSTS_MFMA" in c and "SQ_INSTS_VALU" in c:
+            lines.append(f"    non-MFMA VALU instructions per MFMA        {(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}")
+        if durs[k]:
+            t = sum(durs[k]) / len(durs[k])
+            lines.append(f"    mean dispatch duration                     {t * 1e3:.3f} ms")
+            lines.append(f"    effective engine clock (active / duration) {gui / t / 1e9:.3f} GHz")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _main(argv):
     if argv[:1] == ["stats"] and "--" in argv:
         i = argv.index("--")
         stats(argv[1], argv[2], " ".join(argv[i + 1:]))
+    elif argv[:1] == ["counters"] and "--" in argv:
+        i = argv.index("--")
+        counters(argv[1], argv[2:i], " ".join(argv[i + 1:]),
+                 kernels={"attn_wide_kernel<128, 8, 1, true>"})
     elif argv[:1] == ["traffic"] and "--" in argv:
         i = argv.index("--")
         cmds = " ".join(argv[i + 1:]).split(" ;; ")
