@@ -67,15 +67,16 @@ static int64_t gcd64(int64_t a, int64_t b) {
   return a;
 }
 
-// Balanced decode plan (see Plan): equal tile-aligned ranges, at most one
-// host boundary inside each. Returns false when the shape does not allow it.
+// Balanced decode plan (see Plan): equal ranges of whole 32-key slices, one
+// per wave (four waves per workgroup, one workgroup per CU), at most one host
+// boundary inside each. Returns false when the shape does not allow it.
 static bool balanced_plan(const Dims& d, int64_t kv_len, Plan* p) {
   if (d.dtype != STAR_BF16 || d.blk % kTile != 0 || d.L % kTile != 0) return false;
   const int64_t groups = (int64_t)d.B * d.Hkv;
-  int64_t w = kNarrowWorkgroups / groups;
+  int64_t w = kDecodeWaves / groups;
   if (w < 1) w = 1;
-  int64_t r = round_up(cdiv(kv_len, w), kTile);
-  if (r < 512) r = 512;
+  int64_t r = round_up(cdiv(kv_len, w), kSlice);
+  if (r < kMinRange) r = kMinRange;
   w = cdiv(kv_len, r);
   int64_t n_split = 0;
   for (int64_t j = 0; j < w; ++j) {

@@ -14,6 +14,9 @@ constexpr int kColsPerWave = 64;      // query columns (row, head pairs) per wav
 constexpr int kNarrowCols = 32;       // columns of the single-tile decode kernel
 constexpr int kTargetWorkgroups = 2048;  // phase-2 planner target, many query rows (8 per CU)
 constexpr int kNarrowWorkgroups = 256;   // phase-2 planner target, decode (one per CU)
+constexpr int kDecodeWaves = 4 * 256;    // balanced plan: ranges per launch (4 waves per CU)
+constexpr int kSlice = 32;               // balanced plan: ranges are whole 32-key slices
+constexpr int kMinRange = 128;           // balanced plan: shortest range
 
 // Everything derived from a validated descriptor.
 struct Dims {
@@ -34,12 +37,13 @@ struct Dims {
 // blk_len rows and the tail into tail_splits of tail_len rows; one workgroup
 // per split.
 //
-// Balanced plan (decode kernel, bf16, tile-aligned blocks): the rows
-// [0, kv_len) of every (sequence, kv head) are cut into n_wg equal ranges of
-// wg_rows rows (a multiple of the tile), one workgroup each, so that the
-// whole grid is resident at once. A range holds at most one host boundary
-// (a block start, or the context/tail edge); a range that holds one yields
-// two splits, one on each side. Splits are numbered in row order.
+// Balanced plan (decode kernel, bf16, tile-aligned blocks and context): the
+// rows [0, kv_len) of every (sequence, kv head) are cut into n_wg equal
+// ranges of wg_rows rows (whole 32-key slices), one wave each, four waves per
+// workgroup, so that the whole grid is resident at once. A range holds at
+// most one host boundary (a block start, or the context/tail edge); a range
+// that holds one yields two splits, one on each side. Splits are numbered in
+// row order.
 struct Plan {
   int32_t narrow;         // 1: single-column-tile decode kernel, 0: wide kernel
   int32_t per_block;      // splits per context block
@@ -50,7 +54,7 @@ struct Plan {
   int32_t n_groups;       // workgroup groups (sequence, kv head[, head sub-group])
   int32_t n_qtiles;       // query-row tiles (wide kernel)
   int32_t balanced;       // 1: balanced plan
-  int32_t n_wg;           // balanced: workgroups (ranges) per group
+  int32_t n_wg;           // balanced: ranges (waves) per group
   int64_t wg_rows;        // balanced: rows per range
   int64_t bnd_period;     // balanced: block starts i*blk with i % bnd_period == 0 fall on a range edge
 };

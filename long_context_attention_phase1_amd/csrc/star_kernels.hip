@@ -780,9 +780,6 @@ struct NarrowArgs {
   // decode step (FUSED kernels only): rows appended at kv_len - n_query
   const uint16_t* k_new;  // [B][n_query][Hkv][D]
   const uint16_t* v_new;
-  // balanced plan (see Plan in star_internal.hpp)
-  int64_t wg_rows, bnd_period;
-  int32_t balanced, n_wg;
 };
 
 // Decode ring: kNarrowStages stages, each one 64-key tile laid out as
@@ -858,10 +855,10 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   using Gm = Geo<D, 4>;
   using Ring = NarrowRing<D>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
-  // after the stream the ring holds the merge area: per split (up to two)
-  // and wave, O as [D][33] (padded: conflict-free both ways), then m and l
-  constexpr int OSM_BYTES = 2 * 4 * D * 33 * 4;
-  static_assert(OSM_BYTES + 2 * 2 * 4 * 32 * 4 <= Ring::BYTES, "merge area must fit in the ring");
+  // after the stream the ring holds the merge area: per wave, O as [D][33]
+  // (padded: conflict-free both ways), then m and l
+  constexpr int OSM_BYTES = 4 * D * 33 * 4;
+  static_assert(OSM_BYTES + 2 * 4 * 32 * 4 <= Ring::BYTES, "merge area must fit in the ring");
   static_assert(Gm::V_AT + Gm::VBYTES <= Ring::BYTES, "edge tiles must fit in the ring");
   static_assert(32 * D * 2 <= Ring::SB, "query tile must fit in one stage");
   __shared__ __attribute__((aligned(1024))) char smem[Ring::BYTES];
@@ -870,29 +867,15 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const int tp = w >> 1, kt = w & 1;  // tile of the pair, 32-key slice of the tile
 
-  // work items in reverse order: the range or split holding the tail (with
-  // its masked edge tiles and the appended rows) starts first instead of
-  // waiting for a CU after the long context ranges
+  // splits in reverse order: the short, partly masked tail splits start
+  // first instead of waiting for a CU after the long context splits
   const int gidx = (int)(blockIdx.x % a.NG);
-  const int32_t jj = (int32_t)(blockIdx.x / a.NG);
+  const int32_t sigma = a.n_split - 1 - (int32_t)(blockIdx.x / a.NG);
   const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
-  // rows [lo, hi) of this workgroup; split sigma, and with the balanced plan a
-  // second split sigma + 1 from the host boundary bnd on (bnd = -1: none)
-  int64_t lo, hi, bnd = -1;
-  int32_t sigma;
-  if (a.balanced) {
-    const int64_t j = (int64_t)a.n_wg - 1 - jj;
-    lo = j * a.wg_rows;
-    hi = lo + a.wg_rows < a.kv_len ? lo + a.wg_rows : a.kv_len;
-    bnd = inner_boundary(a.L, a.blk, a.n_blocks, lo, hi);
-    sigma = (int32_t)(j + inner_boundaries_below(a.L, a.blk, a.n_blocks, a.wg_rows, a.bnd_period,
-                                                 lo));
-  } else {
-    sigma = a.n_split - 1 - jj;
-    int32_t host;
-    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo,
-               &hi, &host);
-  }
+  int64_t lo, hi;
+  int32_t host;
+  split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo, &hi,
+             &host);
   const int64_t pos0 = a.kv_len - a.n_query;
   const int ncols = (int)(a.n_query * a.G);
   // column l32 -> (query j, head)
@@ -932,22 +915,6 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[0][dt] = f32x16{};
   float m[1] = {kMinit}, l[1] = {0.0f};
-  // state of the split before bnd, set aside when this wave reaches bnd
-  f32x16 oprev[1][DT];
-  float mprev = kMinit, lprev = 0.0f;
-  bool switched = false;
-  auto switch_split = [&]() {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      oprev[0][dt] = oacc[0][dt];
-      oacc[0][dt] = f32x16{};
-    }
-    mprev = m[0];
-    lprev = l[0];
-    m[0] = kMinit;
-    l[0] = 0.0f;
-    switched = true;
-  };
 
   u32x4 qop[1][KS];
   auto load_q = [&](u32x4 (&q)[1][KS]) {
@@ -1020,13 +987,10 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     }
     block_sync_lds();
     dma_stage_narrow<D, 4>(smem, Kc + STAR_TOFF(4), Vc + STAR_TOFF(4), lo4, w);
-    // interior tile (relative to i0) where the second split starts
-    const int tb = bnd >= 0 ? (int)(bnd / 64 - i0) : 0x7fffffff;
     // iteration k takes tiles 2k, 2k + 1 from stages (2k) % 5, (2k + 1) % 5
 #define STAR_ITER(S0, S1, K)                                                                  \
   {                                                                                           \
     const int t0 = 2 * (K);                                                                   \
-    if (t0 + tp >= tb && !switched) switch_split();                                           \
     narrow_iteration<D, S0, S1>(smem, lo4, kq, vq, qop, oacc, m, l, c2, t0 + tp < n_int, tp,  \
                                 Kc + STAR_TOFF(t0 + 5), Vc + STAR_TOFF(t0 + 5),               \
                                 Kc + STAR_TOFF(t0 + 6), Vc + STAR_TOFF(t0 + 6), w);           \
@@ -1049,9 +1013,6 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   }
 
   if (n_int == 0) load_q(qop);
-  // edge tiles all lie after bnd (bnd is tile-aligned and precedes every
-  // query position), so they belong to the second split
-  if (bnd >= 0 && !switched) switch_split();
 
   // edge tiles (the causal tail, unaligned ends): waves 0,1, masked
   const int n_edge = (int)(i0 - bf) + (int)(bl - i1);
@@ -1090,54 +1051,320 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     }
   }
 
-  // ---- merge the four waves' (m, l, O) of each split and write the partials
-  // (the ring is idle here: every load has landed and every read is done)
-  const int nsp = bnd >= 0 ? 2 : 1;  // slot 0: split sigma, slot 1: sigma + 1
-  float* osm = (float*)smem;                                      // [2][4][D][33]
-  float* msm = (float*)(smem + OSM_BYTES);                        // [2][4][32]
-  float* lsm = msm + 2 * 4 * 32;                                  // [2][4][32]
-  auto stage_state = [&](int sp, const f32x16 (&oa)[1][DT], float mw, float lraw) {
-    const float lw = pair_sum(lraw);
+  // ---- merge the four waves' (m, l, O) and write the split's partial (the
+  // ring is idle here: every load has landed and every read is done)
+  float* osm = (float*)smem;                   // [4][D][33]: padded, no bank conflicts
+  float* msm = (float*)(smem + OSM_BYTES);     // [4][32]
+  float* lsm = msm + 4 * 32;                   // [4][32]
+  {
+    const float lw = pair_sum(l[0]);
     if (g == 0) {
-      msm[(sp * 4 + w) * 32 + l32] = mw;
-      lsm[(sp * 4 + w) * 32 + l32] = lw;
+      msm[w * 32 + l32] = m[0];
+      lsm[w * 32 + l32] = lw;
     }
     if (cvalid) {
-      float* ow = osm + (sp * 4 + w) * D * 33 + l32;
+      float* ow = osm + w * D * 33 + l32;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ow[(32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)) * 33] = oa[0][dt][i];
+        for (int i = 0; i < 16; ++i) ow[(32 * dt + 8 * (i >> 2) + 4 * g + (i & 3)) * 33] = oacc[0][dt][i];
     }
-  };
-  if (bnd >= 0) {
-    stage_state(0, oprev, mprev, lprev);
-    stage_state(1, oacc, m[0], l[0]);
-  } else {
-    stage_state(0, oacc, m[0], l[0]);
   }
   __syncthreads();
-  const int per = ncols * D;
-  for (int idx = tid; idx < nsp * per; idx += 256) {
-    const int sp = idx / per, rem = idx - sp * per;
-    const int c = rem / D, e = rem - c * D;
-    const float* ms = msm + sp * 4 * 32 + c;
-    const float* ls = lsm + sp * 4 * 32 + c;
-    float M = ms[0];
+  for (int idx = tid; idx < ncols * D; idx += 256) {
+    const int c = idx / D, e = idx - c * D;
+    float M = msm[c];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, ms[ww * 32]);
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, msm[ww * 32 + c]);
     float Ls = 0.0f, O = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float f = fast_exp2((ms[ww * 32] - M) * c2);
-      Ls += f * ls[ww * 32];
-      O += f * osm[((sp * 4 + ww) * D + e) * 33 + c];
+      const float f = fast_exp2((msm[ww * 32 + c] - M) * c2);
+      Ls += f * lsm[ww * 32 + c];
+      O += f * osm[(ww * D + e) * 33 + c];
     }
     const int j = c / a.G, h = kvh * a.G + c % a.G;
-    const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sigma + sp;
+    const int64_t base = (((int64_t)s * a.n_query + j) * a.Hq + h) * a.n_split + sigma;
     const bool any = Ls > 0.0f;
     a.o_part[base * D + e] = any ? O / Ls : 0.0f;
     if (e == 0) a.lse_part[base] = any ? M * a.scale + logf(Ls) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel for the balanced plan: every wave streams one range of the
+// plan (a contiguous run of cache rows of one sequence and kv head) through a
+// ring of its own, two stages of one 32-key slice each ([K rows | V^T
+// columns]), with its own copy of the query tile. No wave waits for another:
+// there is no barrier in the kernel. Each wave writes the partial of its
+// range (two, if the range holds a host boundary) straight from registers.
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q;      // [B][n_query][Hq][D]
+  float* o_part;
+  float* lse_part;
+  const uint16_t* k_new;  // FUSED: [B][n_query][Hkv][D], written at kv_len - n_query
+  const uint16_t* v_new;
+  int64_t rows, L, blk, kv_len, n_query, wg_rows, bnd_period;
+  int32_t n_split, n_blocks, n_wg;  // n_wg: ranges per (sequence, kv head)
+  int32_t Hq, Hkv, G, NG, WPG;      // WPG: workgroups per (sequence, kv head)
+  float scale, c2;
+};
+
+template <int D>
+struct DecodeGeo {
+  static constexpr int CH = D / 8;        // 16-byte chunks per K row
+  static constexpr int RB = 2 * D;        // bytes per K row
+  static constexpr int KB = 32 * RB;      // K rows of a slice
+  static constexpr int VB = D * 64;       // V^T of a slice: D rows x 32 keys
+  static constexpr int SB = KB + VB;      // one stage
+  static constexpr int QB = 32 * D * 2;   // query tile, 32 columns
+  static constexpr int WB = 2 * SB + QB;  // one wave's LDS
+  static constexpr int KI = KB / 1024, VI = VB / 1024, QI = QB / 1024;  // 1-KB loads
+  static constexpr int PER = KI + VI;     // loads per slice
+  static constexpr int KS = D / 16, DT = D / 32;
+};
+
+// LDS byte offset of 16-byte chunk kc (keys 8 kc .. 8 kc + 7 of the slice) of
+// row e of a V^T slice. The XOR with bits 2..3 of e spreads the 16 lanes of
+// one LDS cycle (rows e .. e + 15, one kc) over all banks.
+__device__ __forceinline__ uint32_t vs_off(int e, int kc) {
+  return (uint32_t)(e * 64 + ((kc ^ ((e >> 2) & 3)) << 4));
+}
+
+template <int D, bool FUSED>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
+  using Dg = DecodeGeo<D>;
+  constexpr int KS = Dg::KS, DT = Dg::DT;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * Dg::WB];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  char* ring = smem + w * Dg::WB;   // this wave's two stages
+  char* qsm = ring + 2 * Dg::SB;    // and its query tile
+
+  // the workgroup holding the last ranges (the tail, the appended rows) first
+  const int gidx = (int)(blockIdx.x % a.NG);
+  const int64_t r = (int64_t)(a.WPG - 1 - (int32_t)(blockIdx.x / a.NG)) * 4 + w;
+  if (r >= a.n_wg) return;
+  const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
+  const int64_t lo = r * a.wg_rows;
+  const int64_t hi = lo + a.wg_rows < a.kv_len ? lo + a.wg_rows : a.kv_len;
+  // split sigma from lo; with a host boundary bnd inside, split sigma + 1 from bnd
+  const int64_t bnd = inner_boundary(a.L, a.blk, a.n_blocks, lo, hi);
+  const int32_t sigma =
+      (int32_t)(r + inner_boundaries_below(a.L, a.blk, a.n_blocks, a.wg_rows, a.bnd_period, lo));
+  const int64_t pos0 = a.kv_len - a.n_query;
+  const int ncols = (int)(a.n_query * a.G);
+  const int cj = l32 / a.G, ch = kvh * a.G + l32 % a.G;  // column l32 -> (query, head)
+  const bool cvalid = l32 < ncols;
+  const int64_t cpos = pos0 + cj;
+  const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
+  const uint16_t* K = a.k + head_row0 * D;
+  const uint16_t* V = a.v + head_row0 * D;
+  const float c2 = a.c2;
+
+  if (FUSED) {
+    // append this range's share of the new rows before any of its slices is
+    // loaded (no other wave reads them); the stores complete before the loads
+    const int64_t r0 = pos0 > lo ? pos0 : lo;
+    const int64_t r1 = a.kv_len < hi ? a.kv_len : hi;
+    if (r1 > r0) {
+      uint16_t* Kw = (uint16_t*)K;
+      uint16_t* Vw = (uint16_t*)V;
+      const int n = (int)(r1 - r0);
+      for (int u = lane; u < n * D; u += 64) {
+        const int rr = u / D, e = u % D;
+        const int64_t row = r0 + rr;
+        const int64_t src = (((int64_t)s * a.n_query + (row - pos0)) * a.Hkv + kvh) * D + e;
+        Kw[row * D + e] = a.k_new[src];
+        Vw[(row / 64) * 64 * D + e * 64 + (row % 64)] = a.v_new[src];
+      }
+      wait_vmcnt<0>();
+    }
+  }
+
+  // ---- this wave's load offsets (bytes) inside a slice
+  uint32_t kd[Dg::KI], vd[Dg::VI];
+#pragma unroll
+  for (int j = 0; j < Dg::KI; ++j) {
+    // LDS slot (j * 1024 + 16 lane) / RB of the K slice holds key row swap23(slot)
+    const int slot = j * (1024 / Dg::RB) + lane / Dg::CH;
+    const int c = (lane % Dg::CH) ^ (slot & (Dg::CH - 1));
+    kd[j] = (uint32_t)(swap23(slot) * Dg::RB + 16 * c);
+  }
+#pragma unroll
+  for (int j = 0; j < Dg::VI; ++j) {
+    const int e = 16 * j + lane / 4;
+    const int kc = (lane & 3) ^ ((e >> 2) & 3);
+    vd[j] = (uint32_t)(e * 128 + 16 * kc);  // inside the V^T tile of the slice's 64 rows
+  }
+  // operand offsets: K rows (slot l32, chunk 2 ks + g), V^T rows (32 dt + l32, chunk 2 kb + g)
+  uint32_t kq[KS], vq[2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kq[ks] = k_off<D>(l32, 2 * ks + g);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) vq[kb] = (uint32_t)Dg::KB + vs_off(l32, 2 * kb + g);
+
+  // slices of [lo, hi): [0, n_in) fully visible to every column and inside
+  // [lo, hi); [n_in, n_sl) masked (range end not on a slice, or keys after
+  // the first query position)
+  const int n_sl = (int)((hi - lo + 31) / 32);
+  int64_t vis = pos0 + 1 < hi ? pos0 + 1 : hi;
+  const int n_in = vis > lo ? (int)((vis - lo) / 32) : 0;
+  const int sb = bnd >= 0 ? (int)((bnd - lo) / 32) : 0x7fffffff;  // first slice of split 2
+  const char* Kc = (const char*)K;
+  const char* Vc = (const char*)V;
+  // slice i (clamped to the last one): K rows from row lo + 32 i; V^T from the
+  // 64-row tile holding them, half (lo / 32 + i) & 1
+  auto k_at = [&](int i) -> const char* {
+    i = i < n_sl ? i : n_sl - 1;
+    return Kc + (lo + 32 * (int64_t)i) * Dg::RB;
+  };
+  auto v_at = [&](int i) -> const char* {
+    i = i < n_sl ? i : n_sl - 1;
+    const int64_t row = lo + 32 * (int64_t)i;
+    return Vc + (row / 64) * 64 * Dg::RB + (row % 64) * 2;
+  };
+  auto load_slice = [&](int st, int i) {
+    char* d = ring + st * Dg::SB;
+    const char* kt = k_at(i);
+    const char* vt = v_at(i);
+#pragma unroll
+    for (int j = 0; j < Dg::KI; ++j) dma16_lds(kt, kd[j], d + j * 1024);
+#pragma unroll
+    for (int j = 0; j < Dg::VI; ++j) dma16_lds(vt, vd[j], d + Dg::KB + j * 1024);
+  };
+
+  // ---- query tile: chunk u of this wave's QI loads = column u / CH, chunk
+  // (u % CH) ^ (column & (CH - 1)) at LDS k_off(column, chunk); a column past
+  // ncols loads column 0 and is zeroed when read
+  {
+    const char* qbase = (const char*)(a.q + (int64_t)s * a.n_query * a.Hq * D);
+#pragma unroll
+    for (int i = 0; i < Dg::QI; ++i) {
+      const int col = i * (1024 / Dg::RB) + lane / Dg::CH;
+      const int c = (lane % Dg::CH) ^ (col & (Dg::CH - 1));
+      const int cc = col < ncols ? col : 0;
+      const uint32_t off =
+          (uint32_t)((((cc / a.G) * a.Hq + kvh * a.G + cc % a.G) * D + c * 8) * 2);
+      dma16_lds(qbase, off, qsm + i * 1024);
+    }
+  }
+  load_slice(0, 0);
+  load_slice(1, 1);
+  wait_vmcnt<2 * Dg::PER>();  // the query tile (the oldest loads) has landed
+  asm volatile("" ::: "memory");
+  u32x4 qop[1][KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 v = lds16(qsm + kq[ks]);
+    qop[0][ks] = cvalid ? v : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 oacc[1][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[0][dt] = f32x16{};
+  float m[1] = {kMinit}, l[1] = {0.0f};
+  f32x16 oprev[1][DT];
+  float mprev = kMinit, lprev = 0.0f;
+  bool switched = false;
+
+  auto step = [&](int i, int st) {
+    wait_vmcnt<Dg::PER>();  // slice i has landed; slice i + 1 is in flight
+    asm volatile("" ::: "memory");
+    if (i >= sb && !switched) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        oprev[0][dt] = oacc[0][dt];
+        oacc[0][dt] = f32x16{};
+      }
+      mprev = m[0];
+      lprev = l[0];
+      m[0] = kMinit;
+      l[0] = 0.0f;
+      switched = true;
+    }
+    char* sm = ring + st * Dg::SB;
+    const bool masked = i >= n_in;
+    const int64_t key0 = lo + 32 * (int64_t)i;
+    if (masked) {
+      // keys at or past hi are rows nobody wrote: zero their V^T elements
+      for (int u = lane; u < D * 4; u += 64) {
+        const int e = u / 4, kc = u % 4;
+        u32x4* pc = (u32x4*)(sm + Dg::KB + vs_off(e, kc));
+        *pc = mask_chunk(*pc, key0 + 8 * kc, lo, hi);
+      }
+    }
+    f32x16 sc[1];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sc[0] = mfma_bf16(lds16(sm + kq[ks]), qop[0][ks], ks == 0 ? f32x16{} : sc[0]);
+    if (masked) {
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int64_t key = key0 + acc_key(ii, g);
+        if (key >= hi || key > cpos || !cvalid) sc[0][ii] = -INFINITY;
+      }
+    }
+    float mx[1];
+    slice_max3<1>(sc, mx);
+    rescale_top<1, DT>(mx, m, l, oacc, c2);
+    u32x4 p[1][2];
+    slice_exp2<1>(sc, m, l, p, c2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        oacc[0][dt] = mfma_bf16(lds16(sm + vq[kb] + dt * 32 * 64), p[0][kb], oacc[0][dt]);
+    // this wave's reads of the stage are complete before it is refilled
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    load_slice(st, i + 2);
+  };
+  for (int i = 0; i < n_sl; i += 2) {
+    step(i, 0);
+    if (i + 1 >= n_sl) break;
+    step(i + 1, 1);
+  }
+  wait_vmcnt<0>();
+  // a split that starts at bnd after the last slice is empty
+  if (bnd >= 0 && !switched) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      oprev[0][dt] = oacc[0][dt];
+      oacc[0][dt] = f32x16{};
+    }
+    mprev = m[0];
+    lprev = l[0];
+    m[0] = kMinit;
+    l[0] = 0.0f;
+  }
+
+  // ---- partials straight from registers: column l32's 16 values per dt
+  // tile are rows 32 dt + 8 (i / 4) + 4 g + (i % 4)
+  auto write_split = [&](int32_t sg, const f32x16 (&oa)[1][DT], float mw, float lraw) {
+    const float lt = pair_sum(lraw);
+    if (!cvalid) return;
+    const bool any = lt > 0.0f;
+    const float inv = any ? 1.0f / lt : 0.0f;
+    const int64_t base = (((int64_t)s * a.n_query + cj) * a.Hq + ch) * a.n_split + sg;
+    float* op = a.o_part + base * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *(float4*)(op + 32 * dt + 8 * i4 + 4 * g) =
+            float4{oa[0][dt][4 * i4] * inv, oa[0][dt][4 * i4 + 1] * inv,
+                   oa[0][dt][4 * i4 + 2] * inv, oa[0][dt][4 * i4 + 3] * inv};
+    if (g == 0) a.lse_part[base] = any ? mw * a.scale + logf(lt) : -INFINITY;
+  };
+  if (bnd >= 0) {
+    write_split(sigma, oprev, mprev, lprev);
+    write_split(sigma + 1, oacc, m[0], l[0]);
+  } else {
+    write_split(sigma, oacc, m[0], l[0]);
   }
 }
 
@@ -1257,16 +1484,16 @@ struct MergeArgs {
 };
 
 // One workgroup per (sequence, query, head) row. Thread t owns float4
-// column t % (D/4) of the output and the splits i = t / (D/4) (mod SG): all
-// of its partial loads are issued before the log-sum-exp reductions, so the
-// merge costs one round trip to memory; the SG split groups are summed
-// through LDS at the end.
+// column t % (D/4) of the output and the splits i = t / (D/4) (mod SG): it
+// loads their partials and log-sum-exps into registers at once, so the merge
+// costs one round trip to memory; the split groups are summed through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
   constexpr int C4 = D / 4;       // float4 columns of a row
   constexpr int SG = 256 / C4;    // split groups
-  constexpr int U = 8;            // splits per thread and batch
+  constexpr int U = 24;           // splits per thread and batch
   __shared__ float4 osum[SG][C4];
+  __shared__ float zsum[SG];
   __shared__ float red[4];
   const int t = threadIdx.x, d4 = t % C4, sg = t / C4, lane = t & 63, wv = t >> 6;
   const int64_t row = blockIdx.x;
@@ -1274,12 +1501,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
   const float* lp = a.lse_part + row * n;
   const float4* op = (const float4*)(a.o_part + row * (int64_t)n * D);
   float4 ov[U];
+  float lv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = sg + SG * u;
     ov[u] = i < n ? op[(int64_t)i * C4 + d4] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    lv[u] = i < n ? lp[i] : -INFINITY;
   }
-  // m = max_s lse_s (block reduction)
+  // m = max_s lse_s over every split (block reduction)
   float mx = -INFINITY;
   for (int i = t; i < n; i += 256) mx = fmaxf(mx, lp[i]);
   mx = wave_max(mx);
@@ -1287,60 +1516,45 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const bool empty = mx == -INFINITY;
-  __syncthreads();
-  // z = sum_s exp(lse_s - m)
-  float z = 0.0f;
-  if (!empty)
-    for (int i = t; i < n; i += 256) z += expf(lp[i] - mx);
-  z = wave_sum(z);
-  if (lane == 0) red[wv] = z;
-  __syncthreads();
-  z = (red[0] + red[1]) + (red[2] + red[3]);
-  // o = sum_s exp(lse_s - m) o_s / z
+  // this thread's share of z = sum_s exp(lse_s - m) and of sum_s exp(lse_s - m) o_s
   float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float z = 0.0f;
   if (!empty) {
+    for (int i0 = 0; i0 < n; i0 += SG * U) {
+      if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = sg + SG * u;
-      if (i < n) {
-        const float wgt = expf(lp[i] - mx);
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + sg + SG * u;
+          ov[u] = i < n ? op[(int64_t)i * C4 + d4] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+          lv[u] = i < n ? lp[i] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wgt = expf(lv[u] - mx);  // exp(-inf) = 0 past the last split
+        z += wgt;
         acc.x = fmaf(wgt, ov[u].x, acc.x);
         acc.y = fmaf(wgt, ov[u].y, acc.y);
         acc.z = fmaf(wgt, ov[u].z, acc.z);
         acc.w = fmaf(wgt, ov[u].w, acc.w);
       }
     }
-    for (int i0 = SG * U; i0 < n; i0 += SG * U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + sg + SG * u;
-        ov[u] = i < n ? op[(int64_t)i * C4 + d4] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + sg + SG * u;
-        if (i < n) {
-          const float wgt = expf(lp[i] - mx);
-          acc.x = fmaf(wgt, ov[u].x, acc.x);
-          acc.y = fmaf(wgt, ov[u].y, acc.y);
-          acc.z = fmaf(wgt, ov[u].z, acc.z);
-          acc.w = fmaf(wgt, ov[u].w, acc.w);
-        }
-      }
-    }
   }
   osum[sg][d4] = acc;
+  if (d4 == 0) zsum[sg] = z;
   __syncthreads();
   if (t < C4) {
     float4 o = osum[0][t];
+    float zt = zsum[0];
 #pragma unroll
     for (int k = 1; k < SG; ++k) {
       o.x += osum[k][t].x;
       o.y += osum[k][t].y;
       o.z += osum[k][t].z;
       o.w += osum[k][t].w;
+      zt += zsum[k];
     }
-    const float inv = empty ? 0.0f : 1.0f / z;
+    const float inv = empty ? 0.0f : 1.0f / zt;
     const float v[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
     if (a.o_f32) {
       ((float4*)a.o)[row * C4 + t] = float4{v[0], v[1], v[2], v[3]};
@@ -1350,8 +1564,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
       b.y = pack_bf16(v[2], v[3]);
       ((uint2*)a.o)[row * C4 + t] = b;
     }
+    if (t == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(zt);
   }
-  if (t == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(z);
 }
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
@@ -1455,6 +1669,42 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
   return check_launch();
 }
 
+static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, const void* vc,
+                              int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                              float* lse_part) {
+  DecodeArgs a{};
+  a.k = (const uint16_t*)kc;
+  a.v = (const uint16_t*)vc;
+  a.q = (const uint16_t*)q;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.rows = d.rows;
+  a.L = d.L;
+  a.blk = d.blk;
+  a.kv_len = kv_len;
+  a.n_query = n_query;
+  a.wg_rows = p.wg_rows;
+  a.bnd_period = p.bnd_period;
+  a.n_split = p.n_split;
+  a.n_blocks = d.n_blocks;
+  a.n_wg = p.n_wg;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.NG = d.B * d.Hkv;
+  a.WPG = (p.n_wg + 3) / 4;
+  a.scale = d.scale;
+  a.c2 = d.scale_log2;
+  return a;
+}
+
+template <bool FUSED>
+static void launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.NG * a.WPG));
+  if (d.D == 128) hipLaunchKernelGGL((attn_decode_kernel<128, FUSED>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_decode_kernel<64, FUSED>), grid, dim3(256), 0, st, a);
+}
+
 int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
                           int64_t kv_len, const void* q, int64_t n_query, float* o_part,
                           float* lse_part, void* stream) {
@@ -1473,6 +1723,10 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
     if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(256), 0, st, a);
+    return check_launch();
+  }
+  if (p.narrow && p.balanced) {
+    launch_decode<false>(d, decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part), st);
     return check_launch();
   }
   if (p.narrow) {
@@ -1498,11 +1752,7 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     a.NG = d.B * d.Hkv;
     a.scale = d.scale;
     a.c2 = d.scale_log2;
-    a.balanced = p.balanced;
-    a.n_wg = p.n_wg;
-    a.wg_rows = p.wg_rows;
-    a.bnd_period = p.bnd_period;
-    const dim3 grid((unsigned)((int64_t)a.NG * (p.balanced ? p.n_wg : p.n_split)));
+    const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
     if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, false>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_narrow_kernel<64, false>), grid, dim3(256), 0, st, a);
     return check_launch();
@@ -1548,38 +1798,41 @@ int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t
                        const void* q, const void* k_new, const void* v_new, int64_t n_query,
                        float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
                        void* stream) {
-  NarrowArgs a{};
-  a.k = (const uint16_t*)kc;
-  a.v = (const uint16_t*)vc;
-  a.q = (const uint16_t*)q;
-  a.o_part = o_part;
-  a.lse_part = lse_part;
-  a.rows = d.rows;
-  a.L = d.L;
-  a.blk = d.blk;
-  a.kv_len = kv_len;
-  a.n_query = n_query;
-  a.blk_len = p.blk_len;
-  a.tail_len = p.tail_len;
-  a.per_block = p.per_block;
-  a.n_split = p.n_split;
-  a.n_blocks = d.n_blocks;
-  a.Hq = d.Hq;
-  a.Hkv = d.Hkv;
-  a.G = d.G;
-  a.NG = d.B * d.Hkv;
-  a.scale = d.scale;
-  a.c2 = d.scale_log2;
-  a.k_new = (const uint16_t*)k_new;
-  a.v_new = (const uint16_t*)v_new;
-  a.balanced = p.balanced;
-  a.n_wg = p.n_wg;
-  a.wg_rows = p.wg_rows;
-  a.bnd_period = p.bnd_period;
-  const dim3 grid((unsigned)((int64_t)a.NG * (p.balanced ? p.n_wg : p.n_split)));
   hipStream_t st = (hipStream_t)stream;
-  if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_narrow_kernel<64, true>), grid, dim3(256), 0, st, a);
+  if (p.balanced) {
+    DecodeArgs a = decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part);
+    a.k_new = (const uint16_t*)k_new;
+    a.v_new = (const uint16_t*)v_new;
+    launch_decode<true>(d, a, st);
+  } else {
+    NarrowArgs a{};
+    a.k = (const uint16_t*)kc;
+    a.v = (const uint16_t*)vc;
+    a.q = (const uint16_t*)q;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.rows = d.rows;
+    a.L = d.L;
+    a.blk = d.blk;
+    a.kv_len = kv_len;
+    a.n_query = n_query;
+    a.blk_len = p.blk_len;
+    a.tail_len = p.tail_len;
+    a.per_block = p.per_block;
+    a.n_split = p.n_split;
+    a.n_blocks = d.n_blocks;
+    a.Hq = d.Hq;
+    a.Hkv = d.Hkv;
+    a.G = d.G;
+    a.NG = d.B * d.Hkv;
+    a.scale = d.scale;
+    a.c2 = d.scale_log2;
+    a.k_new = (const uint16_t*)k_new;
+    a.v_new = (const uint16_t*)v_new;
+    const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
+    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_narrow_kernel<64, true>), grid, dim3(256), 0, st, a);
+  }
   const int rc = check_launch();
   if (rc) return rc;
   return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);

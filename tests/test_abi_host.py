@@ -199,14 +199,15 @@ def test_split_plan_covers_cache_once_per_host(case):
 
 @pytest.mark.parametrize("kv_len", [131073, 131072 + 64, 131072 + 320])
 def test_decode_plan_is_balanced_at_128k(kv_len):
-    """Decode at 128K (8 kv heads): every split fits in one of the 32 equal
-    tile-aligned ranges per kv head that keep the grid resident (256 CUs)."""
+    """Decode at 128K (8 kv heads): every split fits in one of the equal
+    32-key-slice ranges, one per wave of a grid of four waves on each of the
+    256 CUs (128 ranges per kv head), so the grid is resident at once."""
     d = _desc(n_q_heads=32, n_kv_heads=8, ctx_len=131072, block_len=16384, anchor_len=16384,
               tail_cap=320)
     n = sa.star_attn_phase2_plan(d, kv_len, 1)
-    r = -(-(-(-kv_len // 32)) // 64) * 64
+    r = -(-(-(-kv_len // 128)) // 32) * 32
     lens = [hi - lo for lo, hi, _ in
             (sa.star_attn_phase2_split_range(d, kv_len, 1, s) for s in range(n))]
     assert max(lens) <= r
-    assert n <= 32 + 9          # 32 ranges, at most one extra split per host boundary
+    assert n <= 128 + 9          # 128 ranges, at most one extra split per host boundary
     assert sum(lens) == kv_len
