@@ -1570,12 +1570,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
 
-// Waves per wide-kernel workgroup: 8 (two per SIMD, 32 columns each) or 4
-// (one per SIMD, 64 columns each).
-#ifndef STAR_WIDE_WAVES
-#define STAR_WIDE_WAVES 8
-#endif
-constexpr int kWideWaves = STAR_WIDE_WAVES;
+// Waves per wide-kernel workgroup: 8, two per SIMD, 32 columns each (four
+// waves of 64 columns need more than the 512 registers of a lane and spill).
+constexpr int kWideWaves = 8;
 
 }  // namespace
 
