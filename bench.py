@@ -221,7 +221,7 @@ def main():
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
     kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true>"
-    kname2 = (f"attn_narrow_kernel<{w.head_dim}, true>", f"lse_merge_kernel<{w.head_dim}>")
+    kname2 = (f"attn_decode_kernel<{w.head_dim}, true>", f"lse_merge_kernel<{w.head_dim}>")
     t1, t2 = load_traffic(kname1), load_traffic(*kname2)
     out = {
         "metric": METRIC,

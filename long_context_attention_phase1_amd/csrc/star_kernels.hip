@@ -5,7 +5,9 @@
 //   attn_wide_kernel    flash-style bf16 MFMA tile loop shared by phase 1
 //                       (anchor pass + local causal pass, normalised bf16
 //                       output) and by phase-2 partials with many query rows
-//   attn_narrow_kernel  split-KV decode partials (<= 32 query columns)
+//   attn_decode_kernel  split-KV decode partials (<= 32 query columns), balanced
+//                       plan: one cache range per wave, no barriers
+//   attn_narrow_kernel  the same for the blockwise plan (unaligned shapes)
 //   attn_f32_kernel     fp32 path (VALU) for both phases
 //   lse_merge_kernel    exact softmax renormalisation of the partials (one
 //                       workgroup per output row)
