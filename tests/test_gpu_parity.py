@@ -44,6 +44,9 @@ CASES = {
     # balanced decode plan: 512-row ranges with a block start (1088) and the
     # tail start (2176) strictly inside, a 16-column query step, tail < 1 tile
     "balanced_bnd": W("balanced_bnd", 1, 8, 2, 128, 2176, 1088, 512, 4, 3, "bf16", seed=15),
+    # per-wave decode kernel at d = 64, two sequences, GQA 8:1, a 24-column
+    # query step; block starts 448 and 1344 fall inside 128-row ranges
+    "balanced_b2_g8_d64": W("bal_b2", 2, 16, 2, 64, 1536, 448, 200, 3, 2, "bf16", seed=16),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
@@ -108,7 +111,7 @@ def test_phase2_query_and_decode_match_oracle(runs, name):
 
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g1_unaligned_a_lt_b", "g2_d64_wide_tail",
                                   "g8_narrow", "f32_gqa_d128", "long_tail_wide",
-                                  "ragged_empty_split", "balanced_bnd"])
+                                  "ragged_empty_split", "balanced_bnd", "balanced_b2_g8_d64"])
 def test_partials_are_the_hosts_replies(runs, name):
     """Each split's (vector, scalar) equals the oracle's host reply on that range."""
     p, _, _, _ = _pipeline(runs, name)
@@ -243,7 +246,7 @@ def test_binding_rejects_wrong_buffers():
 
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g8_narrow", "peaked", "ragged_empty_split",
                                   "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks",
-                                  "balanced_bnd"])
+                                  "balanced_bnd", "balanced_b2_g8_d64"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
     decode loop and against the three separate calls, every step."""
