@@ -1254,9 +1254,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
       dma16_lds(qbase, off, qsm + i * 1024);
     }
   }
+  // loads are issued for slices inside the range only; every wait below
+  // counts exactly the slices still in flight
   load_slice(0, 0);
-  load_slice(1, 1);
-  wait_vmcnt<2 * Dg::PER>();  // the query tile (the oldest loads) has landed
+  if (n_sl > 1) {
+    load_slice(1, 1);
+    wait_vmcnt<2 * Dg::PER>();  // the query tile (the oldest loads) has landed
+  } else {
+    wait_vmcnt<Dg::PER>();
+  }
   asm volatile("" ::: "memory");
   u32x4 qop[1][KS];
 #pragma unroll
@@ -1274,7 +1280,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   bool switched = false;
 
   auto step = [&](int i, int st) {
-    wait_vmcnt<Dg::PER>();  // slice i has landed; slice i + 1 is in flight
+    // slice i has landed; slice i + 1 (if any) stays in flight
+    if (i + 1 < n_sl) wait_vmcnt<Dg::PER>();
+    else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     if (i >= sb && !switched) {
 #pragma unroll
@@ -1321,9 +1329,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
       for (int kb = 0; kb < 2; ++kb)
         oacc[0][dt] = mfma_bf16(lds16(sm + vq[kb] + dt * 32 * 64), p[0][kb], oacc[0][dt]);
     // this wave's reads of the stage are complete before it is refilled
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    load_slice(st, i + 2);
+    if (i + 2 < n_sl) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      load_slice(st, i + 2);
+    }
   };
   for (int i = 0; i < n_sl; i += 2) {
     step(i, 0);
