@@ -44,16 +44,19 @@ def phase1_flops(w) -> float:
     return 4.0 * w.head_dim * pairs * w.batch * w.n_q_heads
 
 
-def decode_bytes(w, kv_len: int, n_split: int) -> float:
-    """Algorithmic HBM bytes of one decode step (its two launches): the new
-    token's K/V row written, K+V rows [0, kv_len) and the query read once, the
-    fp32 split partials written and read back by the merge, the output row
-    and its LSE written."""
+def decode_bytes(w, kv_len: int) -> float:
+    """Algorithmic HBM bytes of one decode step: the new token's K/V row
+    written, K+V rows [0, kv_len) and the query read once, every host's reply
+    (one fp32 vector and one scalar per query head, for each context block
+    and the tail) written and read back by the aggregation, the output row
+    and its LSE written. The kernels' finer split partials are not counted:
+    they are this implementation's choice, not the method's."""
     elt = 2 if w.dtype == "bf16" else 4
     append = 2.0 * w.batch * w.n_kv_heads * w.head_dim * elt
     kv = 2.0 * w.batch * w.n_kv_heads * kv_len * w.head_dim * elt
     q = w.batch * w.n_q_heads * w.head_dim * elt
-    parts = 2.0 * w.batch * w.n_q_heads * n_split * (w.head_dim + 1) * 4
+    hosts = w.n_blocks + 1
+    parts = 2.0 * w.batch * w.n_q_heads * hosts * (w.head_dim + 1) * 4
     out = w.batch * w.n_q_heads * (w.head_dim * elt + 4)
     return append + kv + q + parts + out
 
@@ -188,7 +191,7 @@ def main():
                                      p.k_tail_rows[row], p.v_tail_rows[row], 1, o_part, lse_part,
                                      o, p.dtype, lse)
             if record:
-                dec_bytes.append(decode_bytes(w, kv_len, n_split))
+                dec_bytes.append(decode_bytes(w, kv_len))
         d1 = ev()
         d1.record(stream)
         return d0, d1
@@ -254,8 +257,8 @@ def main():
                             "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS, "traffic": t2,
                             "kernel": " + ".join(kname2),
                             "algorithmic": "per decode step: K+V rows [0, kv_len) and q read, "
-                                           "new K/V row written, fp32 partials written and "
-                                           "re-read, output row written"},
+                                           "new K/V row written, one fp32 reply per host "
+                                           "written and re-read, output row written"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)

@@ -1,8 +1,10 @@
 """Summaries of rocprofv3 CSV output for the committed profile records.
 
-``python -m long_context_attention_phase1_amd.profiling stats DIR OUT.txt -- CMD``
+``python -m long_context_attention_phase1_amd.profiling stats DIR OUT.txt [BENCH.json] -- CMD``
     formats the kernel_stats.csv of a ``rocprofv3 --kernel-trace --stats
-    --output-format csv`` run (per-kernel calls, total/avg/min/max duration).
+    --output-format csv`` run (per-kernel calls, total/avg/min/max duration)
+    and, given the JSON line that the profiled bench.py printed, the figures
+    of that same run measured with HIP events.
 
 ``python -m long_context_attention_phase1_amd.profiling traffic FETCH_DIR WRITE_DIR OUT``
     reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
@@ -56,7 +58,18 @@ def _find(d: str, suffix: str) -> str:
     return hits[0]
 
 
-def stats(d: str, out: str, command: str) -> None:
+def _bench_lines(path: str):
+    d = json.loads(open(path).read().strip().splitlines()[-1])
+    r1, r2 = d["roofline"], d["roofline_phase2"]
+    return ["# bench.py line printed by the same profiled run (HIP events on the launch stream):",
+            f"#   phase 1 {r1['kernel']}: {r1['achieved']:.1f} TFLOP/s -> "
+            f"{d['phase1_ms']:.2f} ms per launch (median of the timed launches)",
+            f"#   decode loop: {d['decode_us_per_step']:.2f} us per step ({r2['kernel']}), "
+            f"{r2['achieved']:.0f} GB/s",
+            "# raw line: " + json.dumps(d)]
+
+
+def stats(d: str, out: str, command: str, bench_json: str = None) -> None:
     rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}",
              f"# kernel source sha256[:16]: {source_sha()}",
@@ -67,6 +80,8 @@ def stats(d: str, out: str, command: str) -> None:
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
                      f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    if bench_json:
+        lines += _bench_lines(bench_json)
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -185,7 +200,7 @@ def counters(out_txt: str, dirs, command: str, kernels=None) -> None:
 def _main(argv):
     if argv[:1] == ["stats"] and "--" in argv:
         i = argv.index("--")
-        stats(argv[1], argv[2], " ".join(argv[i + 1:]))
+        stats(argv[1], argv[2], " ".join(argv[i + 1:]), argv[3] if i > 3 else None)
     elif argv[:1] == ["counters"] and "--" in argv:
         i = argv.index("--")
         counters(argv[1], argv[2:i], " ".join(argv[i + 1:]),
