@@ -15,6 +15,9 @@ step's two launches: append + partials, merge) divided by the steps. ``cpu_basel
 sample on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+(NAME: a workload of the scope table, default the 128K one, or a sweep
+variant: sweep_128k_b32k, sweep_128k_b8k, sweep_128k_b4k, sweep_128k_a4k_b16k,
+sweep_125k_ragged)
 """
 from __future__ import annotations
 
@@ -151,7 +154,7 @@ def main():
     from long_context_attention_phase1_amd import synthetic as syn
     from tests.gpu_pipeline import Pipeline
 
-    w = syn.WORKLOADS[args.workload]
+    w = syn.workload(args.workload)
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()

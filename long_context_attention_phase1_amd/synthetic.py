@@ -80,6 +80,35 @@ WORKLOADS: Dict[str, Workload] = {
                                  32768, 32768, 128, 128, "bf16"),
 }
 
+# Variants of the 128K workload that the pages discuss, as performance
+# sweeps (same heads, inputs and peaked rows; 64 decode steps): the block
+# fractions L/4, L/16 and L/32 beside the L/8 of the 128K workload (paperhub.cn
+# review page, reply to reviewer x5MA point 3), an anchor shorter than the
+# block (reply to EMsM point 5: the anchor is at most one block), and a
+# context that is a multiple of neither the block nor the 64-row cache tile
+# (ragged last block, unaligned edges).
+_C3 = WORKLOADS["llama8b_128k_peaked"]
+SWEEPS: Dict[str, Workload] = {
+    "sweep_128k_b32k": _C3.replace(name="sweep_128k_b32k", block_len=32768, anchor_len=32768,
+                                   n_decode=64),
+    "sweep_128k_b8k": _C3.replace(name="sweep_128k_b8k", block_len=8192, anchor_len=8192,
+                                  n_decode=64),
+    "sweep_128k_b4k": _C3.replace(name="sweep_128k_b4k", block_len=4096, anchor_len=4096,
+                                  n_decode=64),
+    "sweep_128k_a4k_b16k": _C3.replace(name="sweep_128k_a4k_b16k", anchor_len=4096,
+                                       n_decode=64),
+    "sweep_125k_ragged": _C3.replace(name="sweep_125k_ragged", ctx_len=125003, n_decode=64),
+}
+
+
+def workload(name: str) -> Workload:
+    """A workload of the scope table or a sweep variant, by name."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name in SWEEPS:
+        return SWEEPS[name]
+    raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS) + sorted(SWEEPS)}")
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest-even); returns the uint16 bit patterns.

@@ -13,6 +13,7 @@ import pytest
 
 import long_context_attention_phase1_amd as sa
 from long_context_attention_phase1_amd import binding as B
+from long_context_attention_phase1_amd import synthetic as syn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "star_attn.h")
@@ -166,6 +167,12 @@ PLAN_CASES = [
     (1, 16, 2, 256, 64, 64, 6, 256 + 4, 4),
     (1, 8, 2, 300, 7, 3, 2000, 300 + 1999, 1999),
 ]
+# the sweep variants at their query step and their first and last decode steps
+for _w in syn.SWEEPS.values():
+    for _kv, _nq in ((_w.ctx_len + _w.n_query, _w.n_query), (_w.ctx_len + _w.n_query + 1, 1),
+                     (_w.ctx_len + _w.tail_cap, 1)):
+        PLAN_CASES.append((_w.batch, _w.n_q_heads, _w.n_kv_heads, _w.ctx_len, _w.block_len,
+                           _w.anchor_len, _w.tail_cap, _kv, _nq))
 
 
 @pytest.mark.parametrize("case", PLAN_CASES)

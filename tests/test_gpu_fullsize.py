@@ -1,4 +1,5 @@
-"""GPU parity at the full sizes of the four bf16 workloads of the scope table.
+"""GPU parity at the full sizes of the four bf16 workloads of the scope table
+and of the sweep variants of the 128K workload.
 
 Each workload runs on the GPU exactly as bench.py times it: context
 kv_write, phase 1, the query step (kv_write + partials + merge), then every
@@ -29,7 +30,9 @@ from tests.gpu_pipeline import Pipeline, to_host_f64
 pytestmark = pytest.mark.gpu
 
 TOL_O, TOL_LSE = 2e-2, 2e-3
-FULL = ["llama8b_32k", "llama8b_128k_peaked", "llama8b_1m", "llama70b_256k_b4"]
+# the four bf16 workloads of the scope table, then the sweep variants (block
+# fractions, a shorter anchor, a ragged unaligned context)
+FULL = ["llama8b_32k", "llama8b_128k_peaked", "llama8b_1m", "llama70b_256k_b4"] + list(syn.SWEEPS)
 
 
 def _ctx_rows(w, rng, n_random=4):
@@ -53,7 +56,7 @@ def _tail_rows(w):
 def test_full_size_sampled_parity(name):
     if not torch.cuda.is_available():
         pytest.skip("no GPU in this environment")
-    w = syn.WORKLOADS[name]
+    w = syn.workload(name)
     threads = min(16, os.cpu_count() or 1)
     p = Pipeline(w, threads=threads, fill_nan=False)
     p.write_context()

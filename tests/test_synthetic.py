@@ -1,5 +1,6 @@
 """The seeded input generator: determinism, seekability, rounding, peaked rows."""
 import numpy as np
+import pytest
 import torch
 
 from long_context_attention_phase1_amd import synthetic as syn
@@ -62,3 +63,27 @@ def test_f32_workload_values():
     assert x.dtype == np.float32 and x.shape == (1, 512, 1, 64)
     t = syn.full_tensor(w, syn.T_QTAIL)
     assert t.shape == (1, 24, 1, 64)
+
+
+def test_sweeps_vary_only_the_intended_sizes():
+    """Each sweep variant is the 128K workload with only its block sizes (or
+    context length) changed and 64 decode steps; lookup by name covers both
+    tables."""
+    base = syn.WORKLOADS["llama8b_128k_peaked"]
+    changed = {
+        "sweep_128k_b32k": {"block_len": 32768, "anchor_len": 32768},
+        "sweep_128k_b8k": {"block_len": 8192, "anchor_len": 8192},
+        "sweep_128k_b4k": {"block_len": 4096, "anchor_len": 4096},
+        "sweep_128k_a4k_b16k": {"anchor_len": 4096},
+        "sweep_125k_ragged": {"ctx_len": 125003},
+    }
+    assert set(changed) == set(syn.SWEEPS)
+    for name, kw in changed.items():
+        w = syn.workload(name)
+        assert w == base.replace(name=name, n_decode=64, **kw)
+        assert w.anchor_len <= w.block_len
+    r = syn.workload("sweep_125k_ragged")
+    assert r.ctx_len % r.block_len != 0 and r.ctx_len % 64 != 0 and r.n_blocks == 8
+    assert syn.workload("llama8b_32k") is syn.WORKLOADS["llama8b_32k"]
+    with pytest.raises(KeyError):
+        syn.workload("nope")
