@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--workload", default="llama8b_128k_peaked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=None)
+    ap.add_argument("--paged", action="store_true",
+                    help="phase 2 (query step and decode loop) on a paged cache through a "
+                         "block table; the context is written into the pages too")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -152,7 +155,7 @@ def main():
 
     import long_context_attention_phase1_amd as sa
     from long_context_attention_phase1_amd import synthetic as syn
-    from tests.gpu_pipeline import Pipeline
+    from tests.gpu_pipeline import PagedPipeline, Pipeline
 
     w = syn.workload(args.workload)
     torch.cuda.set_device(0)
@@ -160,7 +163,7 @@ def main():
         copy_calibration()
     t_gen = time.perf_counter()
     inputs = syn.make_inputs(w, args.threads)
-    p = Pipeline(w, inputs=inputs, fill_nan=False)
+    p = (PagedPipeline if args.paged else Pipeline)(w, inputs=inputs, fill_nan=False)
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
@@ -189,10 +192,8 @@ def main():
             kv_len = w.ctx_len + row + 1
             n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
             # append the token's K/V + split partials (one launch), then the
-            # merge (a second launch)
-            sa.star_attn_decode_step(p.desc, p.k_cache, p.v_cache, kv_len, p.q_tail_rows[row],
-                                     p.k_tail_rows[row], p.v_tail_rows[row], 1, o_part, lse_part,
-                                     o, p.dtype, lse)
+            # merge (a second launch): star_attn_decode_step[_paged]
+            p.decode_call(kv_len, row, o_part, lse_part, o, lse)
             if record:
                 dec_bytes.append(decode_bytes(w, kv_len))
         d1 = ev()
@@ -226,8 +227,9 @@ def main():
     dec_gbs = float(np.sum(dec_bytes) / (np.sum(loop_ms) * 1e-3) / 1e9)
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
-    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true>"
-    kname2 = (f"attn_decode_kernel<{w.head_dim}, true>", f"lse_merge_kernel<{w.head_dim}>")
+    pg = "true" if args.paged else "false"
+    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false>"
+    kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}>", f"lse_merge_kernel<{w.head_dim}>")
     t1, t2 = load_traffic(kname1), load_traffic(*kname2)
     out = {
         "metric": METRIC,
@@ -246,7 +248,8 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx_len": w.ctx_len,
                    "block_len": w.block_len, "anchor_len": w.anchor_len,
                    "n_query": w.n_query, "n_decode": w.n_decode,
-                   "peaked_k_rows": w.peak_frac, "peak_factor": w.peak_factor},
+                   "peaked_k_rows": w.peak_frac, "peak_factor": w.peak_factor,
+                   "phase2_cache": "paged" if args.paged else "contiguous"},
         "phase1_ms": p1_ms,
         "phase1_ctx_tokens_per_s": ctx_tok_s,
         "query_step_ms": q_ms,

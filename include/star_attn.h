@@ -205,6 +205,50 @@ int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cac
                           int64_t n_query, float* o_part, float* lse_part, void* o,
                           int32_t o_dtype, float* lse_out, void* stream);
 
+/*
+ * Paged KV cache (paperhub.cn rebuttal, reply to reviewer dKGV point 3,
+ * serving frameworks: a paged memory manager can hold each host's local KV
+ * cache). The same phase-2 operations with the cache kept in pages of
+ * STAR_KV_TILE rows, found through a block table; phase 1 reads the
+ * contiguous cache described above.
+ *   k_pages, v_pages  pools of pages; page p holds, for every kv head g,
+ *                the tile in the contiguous layout's form:
+ *                K element (p, g, r, e): K[((p*Hkv + g)*64 + r)*d + e]
+ *                V element (p, g, r, e): V[((p*Hkv + g)*64)*d + e*64 + r]
+ *                (star_kv_page_bytes() bytes per page and per pool)
+ *   block_table  device int32 [batch][max_pages]: entry [s][t] is the page
+ *                holding rows [64t, 64t + 64) of sequence s.
+ *                max_pages >= ceil((ctx_len + tail_cap) / 64) (else
+ *                STAR_ERR_SHAPE). Every entry for rows a call reads or writes
+ *                must be a valid page of the pools; the library cannot check
+ *                device memory, and an invalid id is undefined behaviour.
+ *                Sequences may share pages they only read (a common prefix);
+ *                rows that are written must not share a page with rows
+ *                another sequence or call reads at the same time.
+ * Results are bit-identical to the contiguous-cache calls on the same
+ * values: only the addresses differ.
+ */
+size_t star_kv_page_bytes(const star_attn_desc* desc);
+
+/* star_kv_write through the block table (same arguments, checks and copy). */
+int star_kv_write_paged(const star_attn_desc* desc, void* k_pages, void* v_pages,
+                        const int32_t* block_table, int32_t max_pages, int64_t pos0,
+                        const void* k_src, const void* v_src, int64_t n_tok, void* stream);
+
+/* star_attn_phase2_partial on the paged cache (same plan and outputs). */
+int star_attn_phase2_partial_paged(const star_attn_desc* desc, const void* k_pages,
+                                   const void* v_pages, const int32_t* block_table,
+                                   int32_t max_pages, int64_t kv_len, const void* q,
+                                   int64_t n_query, float* o_part, float* lse_part,
+                                   void* stream);
+
+/* star_attn_decode_step on the paged cache (same steps, launches and outputs). */
+int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void* v_pages,
+                                const int32_t* block_table, int32_t max_pages, int64_t kv_len,
+                                const void* q, const void* k_new, const void* v_new,
+                                int64_t n_query, float* o_part, float* lse_part, void* o,
+                                int32_t o_dtype, float* lse_out, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* star_attn_strerror(int status);
 

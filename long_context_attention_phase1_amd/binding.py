@@ -31,7 +31,9 @@ STAR_KV_TILE = 64
 
 EXPORTS = ("star_kv_cache_bytes", "star_kv_write", "star_attn_phase1", "star_attn_phase2_plan",
            "star_attn_phase2_split_range", "star_attn_phase2_partial", "star_attn_lse_merge",
-           "star_attn_decode_step", "star_attn_strerror", "star_attn_abi_version")
+           "star_attn_decode_step", "star_kv_page_bytes", "star_kv_write_paged",
+           "star_attn_phase2_partial_paged", "star_attn_decode_step_paged", "star_attn_strerror",
+           "star_attn_abi_version")
 
 
 class StarAttnError(RuntimeError):
@@ -73,6 +75,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "star_attn_phase2_partial": (ctypes.c_int, [D, P, P, I64, P, I64, P, P, P]),
         "star_attn_lse_merge": (ctypes.c_int, [D, I64, I32, P, P, P, I32, P, P]),
         "star_attn_decode_step": (ctypes.c_int, [D, P, P, I64, P, P, P, I64, P, P, P, I32, P, P]),
+        "star_kv_page_bytes": (ctypes.c_size_t, [D]),
+        "star_kv_write_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, P, I64, P]),
+        "star_attn_phase2_partial_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, I64, P, P, P]),
+        "star_attn_decode_step_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, P, P, I64, P, P, P,
+                                                       I32, P, P]),
         "star_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "star_attn_abi_version": (ctypes.c_int, []),
     }
@@ -246,3 +253,91 @@ def star_attn_decode_step(desc, k_cache, v_cache, kv_len: int, q, k_new, v_new, 
         _ptr(v_new, shp_kv, elt, "v_new"), n_query, _ptr(o_part, shp_p, f32, "o_part"),
         _ptr(lse_part, shp_p[:4], f32, "lse_part"), _ptr(o, shp_q, od, "o"), o_dtype, _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
     _check(st, "star_attn_decode_step")
+
+
+# ---------------------------------------------------------------- paged cache
+
+def star_kv_page_bytes(desc: StarAttnDesc) -> int:
+    return load_library().star_kv_page_bytes(ctypes.byref(desc))
+
+
+def alloc_kv_pages(desc: StarAttnDesc, n_pages: int, device="cuda"):
+    """A pool of n_pages K (or V) pages (torch.empty of n_pages * star_kv_page_bytes)."""
+    torch = _torch()
+    nbytes = star_kv_page_bytes(desc)
+    if nbytes == 0 or n_pages < 1:
+        raise StarAttnError(STAR_ERR_INVALID_ARG, "alloc_kv_pages")
+    elt = _elt(desc)
+    return torch.empty(n_pages * nbytes // torch.tensor([], dtype=elt).element_size(), dtype=elt,
+                       device=device)
+
+
+def _pages_ptr(desc, x, name):
+    if isinstance(x, int) or x is None:
+        return x
+    nbytes = star_kv_page_bytes(desc)
+    size = x.numel() * x.element_size()
+    if nbytes == 0 or size < nbytes or size % nbytes:
+        raise ValueError(f"{name}: {size} bytes is not a whole number of {nbytes}-byte pages")
+    return _ptr(x, dtype=_elt(desc), name=name)
+
+
+def _table(desc, block_table):
+    """(pointer, max_pages) of a device int32 [batch][max_pages] table, or a
+    (pointer, max_pages) pair passed through."""
+    if isinstance(block_table, tuple):
+        return block_table
+    torch = _torch()
+    if block_table.dim() != 2 or block_table.shape[0] != desc.batch:
+        raise ValueError(f"block_table: shape {tuple(block_table.shape)}, expected "
+                         f"({desc.batch}, max_pages)")
+    return _ptr(block_table, dtype=torch.int32, name="block_table"), int(block_table.shape[1])
+
+
+def star_kv_write_paged(desc, k_pages, v_pages, block_table, pos0: int, k_src, v_src, n_tok: int,
+                        stream=None):
+    shp = (desc.batch, n_tok, desc.n_kv_heads, desc.head_dim)
+    elt = None if isinstance(k_src, int) else _elt(desc)
+    tp, mp = _table(desc, block_table)
+    st = load_library().star_kv_write_paged(
+        ctypes.byref(desc), _pages_ptr(desc, k_pages, "k_pages"), _pages_ptr(desc, v_pages, "v_pages"),
+        tp, mp, pos0, _ptr(k_src, shp, elt, "k_src"), _ptr(v_src, shp, elt, "v_src"), n_tok,
+        _stream(stream))
+    _check(st, "star_kv_write_paged")
+
+
+def star_attn_phase2_partial_paged(desc, k_pages, v_pages, block_table, kv_len: int, q,
+                                   n_query: int, o_part, lse_part, stream=None):
+    torch = None if isinstance(q, int) else _torch()
+    n_split = star_attn_phase2_plan(desc, kv_len, n_query)
+    shp_q = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    shp_o = (desc.batch, n_query, desc.n_q_heads, n_split, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    tp, mp = _table(desc, block_table)
+    st = load_library().star_attn_phase2_partial_paged(
+        ctypes.byref(desc), _pages_ptr(desc, k_pages, "k_pages"), _pages_ptr(desc, v_pages, "v_pages"),
+        tp, mp, kv_len, _ptr(q, shp_q, None if torch is None else _elt(desc), "q"), n_query,
+        _ptr(o_part, shp_o, f32, "o_part"), _ptr(lse_part, shp_o[:4], f32, "lse_part"),
+        _stream(stream))
+    _check(st, "star_attn_phase2_partial_paged")
+
+
+def star_attn_decode_step_paged(desc, k_pages, v_pages, block_table, kv_len: int, q, k_new, v_new,
+                                n_query: int, o_part, lse_part, o, o_dtype: int, lse_out=None,
+                                stream=None):
+    torch = None if isinstance(q, int) else _torch()
+    n_split = star_attn_phase2_plan(desc, kv_len, n_query)
+    shp_q = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    shp_kv = (desc.batch, n_query, desc.n_kv_heads, desc.head_dim)
+    shp_p = (desc.batch, n_query, desc.n_q_heads, n_split, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    elt = None if torch is None else _elt(desc)
+    od = None if torch is None else (torch.bfloat16 if o_dtype == STAR_BF16 else torch.float32)
+    tp, mp = _table(desc, block_table)
+    st = load_library().star_attn_decode_step_paged(
+        ctypes.byref(desc), _pages_ptr(desc, k_pages, "k_pages"), _pages_ptr(desc, v_pages, "v_pages"),
+        tp, mp, kv_len, _ptr(q, shp_q, elt, "q"), _ptr(k_new, shp_kv, elt, "k_new"),
+        _ptr(v_new, shp_kv, elt, "v_new"), n_query, _ptr(o_part, shp_p, f32, "o_part"),
+        _ptr(lse_part, shp_p[:4], f32, "lse_part"), _ptr(o, shp_q, od, "o"), o_dtype,
+        _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
+    _check(st, "star_attn_decode_step_paged")

@@ -235,6 +235,82 @@ int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cac
   return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }
 
+// ---- paged cache: the same entry points, the cache read and written through a
+// block table
+
+size_t star_kv_page_bytes(const star_attn_desc* desc) {
+  Dims d;
+  if (validate_desc(desc, &d) != STAR_OK) return 0;
+  const size_t elt = d.dtype == STAR_BF16 ? 2 : 4;
+  return (size_t)d.Hkv * STAR_KV_TILE * d.D * elt;
+}
+
+// The page pools and a table that covers every row of the cache's capacity.
+static int validate_pages(const Dims& d, const void* k_pages, const void* v_pages,
+                          const int32_t* table, int32_t max_pages) {
+  if (!k_pages || !v_pages || !table) return STAR_ERR_INVALID_ARG;
+  if (max_pages < (d.L + d.tail_cap + STAR_KV_TILE - 1) / STAR_KV_TILE) return STAR_ERR_SHAPE;
+  return STAR_OK;
+}
+
+int star_kv_write_paged(const star_attn_desc* desc, void* k_pages, void* v_pages,
+                        const int32_t* block_table, int32_t max_pages, int64_t pos0,
+                        const void* k_src, const void* v_src, int64_t n_tok, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_src || !v_src || n_tok < 1) return STAR_ERR_INVALID_ARG;
+  st = validate_pages(d, k_pages, v_pages, block_table, max_pages);
+  if (st) return st;
+  if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  return launch_kv_write(d, k_pages, v_pages, pos0, k_src, v_src, n_tok, stream, block_table,
+                         max_pages);
+}
+
+int star_attn_phase2_partial_paged(const star_attn_desc* desc, const void* k_pages,
+                                   const void* v_pages, const int32_t* block_table,
+                                   int32_t max_pages, int64_t kv_len, const void* q,
+                                   int64_t n_query, float* o_part, float* lse_part, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!q || !o_part || !lse_part) return STAR_ERR_INVALID_ARG;
+  st = validate_pages(d, k_pages, v_pages, block_table, max_pages);
+  if (st) return st;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  return launch_phase2_partial(d, p, k_pages, v_pages, kv_len, q, n_query, o_part, lse_part,
+                               stream, block_table, max_pages);
+}
+
+int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void* v_pages,
+                                const int32_t* block_table, int32_t max_pages, int64_t kv_len,
+                                const void* q, const void* k_new, const void* v_new,
+                                int64_t n_query, float* o_part, float* lse_part, void* o,
+                                int32_t o_dtype, float* lse_out, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!q || !k_new || !v_new || !o_part || !lse_part || !o) return STAR_ERR_INVALID_ARG;
+  if (o_dtype != STAR_BF16 && o_dtype != STAR_F32) return STAR_ERR_DTYPE;
+  st = validate_pages(d, k_pages, v_pages, block_table, max_pages);
+  if (st) return st;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  if (p.narrow && d.dtype == STAR_BF16)
+    return launch_decode_step(d, p, k_pages, v_pages, kv_len, q, k_new, v_new, n_query, o_part,
+                              lse_part, o, o_dtype, lse_out, stream, block_table, max_pages);
+  st = launch_kv_write(d, k_pages, v_pages, kv_len - n_query, k_new, v_new, n_query, stream,
+                       block_table, max_pages);
+  if (st) return st;
+  st = launch_phase2_partial(d, p, k_pages, v_pages, kv_len, q, n_query, o_part, lse_part, stream,
+                             block_table, max_pages);
+  if (st) return st;
+  return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
+}
+
 const char* star_attn_strerror(int status) {
   switch (status) {
     case STAR_OK: return "success";

@@ -145,17 +145,21 @@ static inline void split_range(const Dims& d, const Plan& p, int64_t kv_len, int
 }
 
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
+// table / maxp: a paged cache (kc, vc the page pools; table [B][maxp] page
+// ids), or null / 0 for the contiguous cache.
 int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
-                    const void* vs, int64_t n_tok, void* stream);
+                    const void* vs, int64_t n_tok, void* stream, const int32_t* table = nullptr,
+                    int32_t maxp = 0);
 int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
                   void* stream);
 int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
                           int64_t kv_len, const void* q, int64_t n_query, float* o_part,
-                          float* lse_part, void* stream);
+                          float* lse_part, void* stream, const int32_t* table = nullptr,
+                          int32_t maxp = 0);
 int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
                        const void* q, const void* k_new, const void* v_new, int64_t n_query,
                        float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
-                       void* stream);
+                       void* stream, const int32_t* table = nullptr, int32_t maxp = 0);
 int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const float* o_part,
                      const float* lse_part, void* o, int32_t o_dtype, float* lse_out,
                      void* stream);

@@ -117,6 +117,50 @@ __device__ __forceinline__ u32x4 load_v_chunk(const uint16_t* p, int64_t k0, int
   return mask_chunk(ld16(p), k0, lo, hi);
 }
 
+// ---- cache addressing ---------------------------------------------------------
+//
+// Tile t of sequence s and kv head g (cache rows [64t, 64t + 64)) begins at
+// the same element offset in the K and in the V buffer: a K tile ([64][D],
+// rows) and a transposed V tile ([D][64]) both hold 64 * D elements.
+// Contiguous cache: the R / 64 tiles of (s, g) follow each other. Paged
+// cache: tile t of sequence s lives in page table[s][t]; a page holds that
+// tile for every kv head, kv head g at element (page * Hkv + g) * 64 * D.
+struct PageMap {
+  const int32_t* table;  // [B][maxp] page ids; null: contiguous cache
+  int32_t maxp;
+};
+
+template <bool PAGED, int D>
+__device__ __forceinline__ int64_t tile_elem(const PageMap& pm, int64_t rows, int Hkv, int s, int g,
+                                             int64_t t) {
+  if constexpr (PAGED) return ((int64_t)pm.table[(int64_t)s * pm.maxp + t] * Hkv + g) * (64 * D);
+  else return (((int64_t)s * Hkv + g) * rows + 64 * t) * D;
+}
+
+// The same for a tile index that is uniform across the wave. The table is
+// read-only while a kernel runs, so it is read through the constant address
+// space: a uniform address then gives a scalar load, which the direct-to-LDS
+// loads' vmcnt accounting never sees (a vector load would need a vmcnt wait
+// that drains them).
+typedef const __attribute__((address_space(4))) int32_t* const_table_ptr;
+
+// Page id of tile t of sequence s (t wave-uniform), by a scalar load.
+__device__ __forceinline__ int32_t page_u(const PageMap& pm, int s, int64_t t) {
+  const uint64_t ad = (uint64_t)(uintptr_t)(pm.table + ((int64_t)s * pm.maxp + t));
+  const uint32_t alo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ad);
+  const uint32_t ahi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ad >> 32));
+  return *(const_table_ptr)(uintptr_t)(((uint64_t)ahi << 32) | (uint64_t)alo);
+}
+template <bool PAGED, int D>
+__device__ __forceinline__ int64_t tile_elem_u(const PageMap& pm, int64_t rows, int Hkv, int s,
+                                               int g, int64_t t) {
+  if constexpr (PAGED) {
+    return ((int64_t)page_u(pm, s, t) * Hkv + g) * (64 * D);
+  } else {
+    return tile_elem<false, D>(pm, rows, Hkv, s, g, t);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // kv_write
 // ---------------------------------------------------------------------------
@@ -125,11 +169,12 @@ struct KvArgs {
   void* vc;
   const void* ks;
   const void* vs;
+  PageMap pm;
   int64_t pos0, n_tok, rows, t0;
   int32_t Hkv, nt;
 };
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
   constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;              // chunks per row
@@ -141,7 +186,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
   const int64_t r0 = tile * 64;
   const int64_t r_lo = a.pos0 > r0 ? a.pos0 : r0;
   const int64_t r_hi = (a.pos0 + a.n_tok) < (r0 + 64) ? (a.pos0 + a.n_tok) : (r0 + 64);
-  const int64_t head_row0 = ((int64_t)s * a.Hkv + g) * a.rows;
+  // this tile's first element in the K and the V buffer
+  const int64_t tb = tile_elem<PAGED, D>(a.pm, a.rows, a.Hkv, s, g, tile);
   T* kc = (T*)a.kc;
   T* vc = (T*)a.vc;
   const T* ks = (const T*)a.ks;
@@ -151,12 +197,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
     const int64_t r = r0 + rr;
     if (r >= r_lo && r < r_hi) {
       const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
-      *(u32x4*)(kc + (head_row0 + r) * D + c * VEC) = *(const u32x4*)(ks + src);
+      *(u32x4*)(kc + tb + rr * D + c * VEC) = *(const u32x4*)(ks + src);
       *(u32x4*)(&vsm[rr][c * VEC]) = *(const u32x4*)(vs + src);
     }
   }
   __syncthreads();
-  T* vt = vc + (head_row0 + r0) * D;  // transposed tile: element (e, kk) at e*64 + kk
+  T* vt = vc + tb;  // transposed tile: element (e, kk) at e*64 + kk
   if (r_lo == r0 && r_hi == r0 + 64) {
     constexpr int KC = 64 / VEC;
     for (int u = tid; u < D * KC; u += 256) {
@@ -194,6 +240,7 @@ struct WideArgs {
   int32_t Hq, Hkv, G, HW, HQ, NG, NRT;  // NRT: row tiles (phase 1) / query tiles (phase 2)
   int32_t BM;                           // rows per workgroup = 64 * (4 / HW)
   float scale, c2;                      // softmax scale and scale*log2(e)
+  PageMap pm;                           // phase 2 on a paged cache
 };
 
 // Online-softmax update of one query-column tile from raw scores s[kt]
@@ -311,18 +358,20 @@ struct EdgeTile {
   static constexpr int VPT = D * 8 / Gm::NT;
   u32x4 kr[KPT], vr[VPT];
 
-  __device__ __forceinline__ void load(const uint16_t* K, const uint16_t* V, int64_t kbase,
+  // Kt, Vt: the tile holding keys [kbase, kbase + 64)
+  __device__ __forceinline__ void load(const uint16_t* Kt, const uint16_t* Vt, int64_t kbase,
                                        int64_t lo, int64_t hi, int tid) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int u = tid + Gm::NT * i, slot = u / Gm::CH, c = u % Gm::CH;
-      const int64_t key = kbase + (slot & 32) + swap23(slot & 31);
-      kr[i] = (key >= lo && key < hi) ? ld16(K + key * D + c * 8) : u32x4{0, 0, 0, 0};
+      const int kk = (slot & 32) + swap23(slot & 31);
+      const int64_t key = kbase + kk;
+      kr[i] = (key >= lo && key < hi) ? ld16(Kt + kk * D + c * 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int u = tid + Gm::NT * i, e = u >> 3, kc = u & 7;
-      vr[i] = load_v_chunk(V + kbase * D + e * 64 + kc * 8, kbase + kc * 8, lo, hi);
+      vr[i] = load_v_chunk(Vt + e * 64 + kc * 8, kbase + kc * 8, lo, hi);
     }
   }
   __device__ __forceinline__ void store(char* smem, int tid) const {
@@ -541,8 +590,9 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
 
 // Wave -> columns: wave w owns QT column tiles of 32 (query row, head) pairs.
 // The workgroup covers 256 columns: HW heads of one kv head x 64*(4/HW) rows.
-template <int D, int NW, int QT, bool PHASE1>
+template <int D, int NW, int QT, bool PHASE1, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
+  static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
   using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
   constexpr int WPR = 2 / QT;  // waves per 64-row sub-tile of one head
@@ -595,8 +645,13 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   }
   const int64_t wrow0 = row0 + rw * 64 + wsub * 32 * QT;  // this wave's first query row
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
-  const uint16_t* K = a.k + head_row0 * D;
-  const uint16_t* V = a.v + head_row0 * D;
+  const uint16_t* K = PAGED ? a.k : a.k + head_row0 * D;
+  const uint16_t* V = PAGED ? a.v : a.v + head_row0 * D;
+  // element offset of this (sequence, kv head)'s tile t from K and from V
+  auto tile_at = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem_u<true, D>(a.pm, a.rows, a.Hkv, s, kvh, t);
+    else return t * 64 * D;
+  };
   const float c2 = a.c2;
 
   // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g
@@ -644,7 +699,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   // interior tile j -> byte offset of its rows (clamped to the last tile)
   auto tile_off = [&](int j) -> int64_t {
     j = j < n_int ? j : n_int - 1;
-    return (j < nAi ? (int64_t)j * 64 : (i0 + (j - nAi)) * 64) * (int64_t)Gm::RB;
+    return tile_at(j < nAi ? (int64_t)j : i0 + (j - nAi)) * 2;
   };
 
   if (n_int > 0) {
@@ -696,7 +751,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
         klo = loB; khi = hiB; causal = true;
       }
       EdgeTile<D, NW> et;
-      et.load(K, V, kbase, klo, khi, tid);
+      et.load(K + tile_at(kbase / 64), V + tile_at(kbase / 64), kbase, klo, khi, tid);
       et.store(smem, tid);
       block_sync_lds();
 #pragma unroll
@@ -782,6 +837,7 @@ struct NarrowArgs {
   // decode step (FUSED kernels only): rows appended at kv_len - n_query
   const uint16_t* k_new;  // [B][n_query][Hkv][D]
   const uint16_t* v_new;
+  PageMap pm;             // paged cache
 };
 
 // Decode ring: kNarrowStages stages, each one 64-key tile laid out as
@@ -852,7 +908,7 @@ __device__ __forceinline__ void narrow_iteration(
 // of the odd tile, each with its own softmax state; the four states are
 // merged through LDS at the end. Sized so one workgroup per CU streams a
 // long contiguous key range with 96-160 KB of loads outstanding.
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool PAGED>
 __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   using Gm = Geo<D, 4>;
   using Ring = NarrowRing<D>;
@@ -886,8 +942,18 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   const int64_t cpos = pos0 + cj;
 
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
-  const uint16_t* K = a.k + head_row0 * D;
-  const uint16_t* V = a.v + head_row0 * D;
+  const uint16_t* K = PAGED ? a.k : a.k + head_row0 * D;
+  const uint16_t* V = PAGED ? a.v : a.v + head_row0 * D;
+  // element offset of this (sequence, kv head)'s tile t from K and from V
+  auto tile_at = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, s, kvh, t);
+    else return t * 64 * D;
+  };
+  // the same for a wave-uniform t (a scalar table read)
+  auto tile_at_u = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem_u<true, D>(a.pm, a.rows, a.Hkv, s, kvh, t);
+    else return t * 64 * D;
+  };
   const float c2 = a.c2;
 
   if (FUSED) {
@@ -903,8 +969,9 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
         const int rr = u / D, e = u % D;
         const int64_t r = r0 + rr;
         const int64_t src = (((int64_t)s * a.n_query + (r - pos0)) * a.Hkv + kvh) * D + e;
-        Kw[r * D + e] = a.k_new[src];
-        Vw[(r / 64) * 64 * D + e * 64 + (r % 64)] = a.v_new[src];
+        const int64_t tb = tile_at(r / 64);
+        Kw[tb + (r % 64) * D + e] = a.k_new[src];
+        Vw[tb + e * 64 + (r % 64)] = a.v_new[src];
       }
       // the stores must complete before this workgroup loads those rows;
       // every other split never reads them
@@ -952,9 +1019,8 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
       vq[kb] = (uint32_t)Gm::KBYTES + v_off(l32, 4 * kt + 2 * kb + g);
     const char* Kc = (const char*)K;
     const char* Vc = (const char*)V;
-    const int64_t base_off = i0 * 64 * (int64_t)Gm::RB;
     const int jmax = n_int - 1;
-#define STAR_TOFF(j) (base_off + (int64_t)((j) < jmax ? (j) : jmax) * 64 * Gm::RB)
+#define STAR_TOFF(j) (tile_at_u(i0 + ((j) < jmax ? (j) : jmax)) * 2)
     const int n_it = (n_int + 1) / 2;
     // the query tile arrives by the same direct-to-LDS loads, into stage 4
     // before that stage's first tile: 16-byte chunk u (lane-major over the
@@ -1022,7 +1088,7 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
     for (int e = 0; e < n_edge; ++e) {
       const int64_t kbase = (e < i0 - bf ? bf + e : i1 + (e - (i0 - bf))) * 64;
       EdgeTile<D, 4> et;
-      et.load(K, V, kbase, lo, hi, tid);
+      et.load(K + tile_at_u(kbase / 64), V + tile_at_u(kbase / 64), kbase, lo, hi, tid);
       et.store(smem, tid);
       block_sync_lds();
       if (tp == 0) {
@@ -1113,6 +1179,7 @@ struct DecodeArgs {
   int32_t n_split, n_blocks, n_wg;  // n_wg: ranges per (sequence, kv head)
   int32_t Hq, Hkv, G, NG, WPG;      // WPG: workgroups per (sequence, kv head)
   float scale, c2;
+  PageMap pm;                       // paged cache
 };
 
 template <int D>
@@ -1136,7 +1203,7 @@ __device__ __forceinline__ uint32_t vs_off(int e, int kc) {
   return (uint32_t)(e * 64 + ((kc ^ ((e >> 2) & 3)) << 4));
 }
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   using Dg = DecodeGeo<D>;
   constexpr int KS = Dg::KS, DT = Dg::DT;
@@ -1163,8 +1230,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   const bool cvalid = l32 < ncols;
   const int64_t cpos = pos0 + cj;
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
-  const uint16_t* K = a.k + head_row0 * D;
-  const uint16_t* V = a.v + head_row0 * D;
+  const uint16_t* K = PAGED ? a.k : a.k + head_row0 * D;
+  const uint16_t* V = PAGED ? a.v : a.v + head_row0 * D;
+  // element offset of this (sequence, kv head)'s tile t from K and from V
+  auto tile_at = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, s, kvh, t);
+    else return t * 64 * D;
+  };
+  // the same for a wave-uniform t (a scalar table read)
+  auto tile_at_u = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem_u<true, D>(a.pm, a.rows, a.Hkv, s, kvh, t);
+    else return t * 64 * D;
+  };
   const float c2 = a.c2;
 
   if (FUSED) {
@@ -1180,8 +1257,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
         const int rr = u / D, e = u % D;
         const int64_t row = r0 + rr;
         const int64_t src = (((int64_t)s * a.n_query + (row - pos0)) * a.Hkv + kvh) * D + e;
-        Kw[row * D + e] = a.k_new[src];
-        Vw[(row / 64) * 64 * D + e * 64 + (row % 64)] = a.v_new[src];
+        const int64_t tb = tile_at(row / 64);
+        Kw[tb + (row % 64) * D + e] = a.k_new[src];
+        Vw[tb + e * 64 + (row % 64)] = a.v_new[src];
       }
       wait_vmcnt<0>();
     }
@@ -1222,22 +1300,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   // 64-row tile holding them, half (lo / 32 + i) & 1
   auto k_at = [&](int i) -> const char* {
     i = i < n_sl ? i : n_sl - 1;
-    return Kc + (lo + 32 * (int64_t)i) * Dg::RB;
+    const int64_t row = lo + 32 * (int64_t)i;
+    return Kc + tile_at_u(row / 64) * 2 + (row % 64) * Dg::RB;
   };
   auto v_at = [&](int i) -> const char* {
     i = i < n_sl ? i : n_sl - 1;
     const int64_t row = lo + 32 * (int64_t)i;
-    return Vc + (row / 64) * 64 * Dg::RB + (row % 64) * 2;
+    return Vc + tile_at_u(row / 64) * 2 + (row % 64) * 2;
   };
-  auto load_slice = [&](int st, int i) {
+  auto load_slice_at = [&](int st, const char* kt, const char* vt) {
     char* d = ring + st * Dg::SB;
-    const char* kt = k_at(i);
-    const char* vt = v_at(i);
 #pragma unroll
     for (int j = 0; j < Dg::KI; ++j) dma16_lds(kt, kd[j], d + j * 1024);
 #pragma unroll
     for (int j = 0; j < Dg::VI; ++j) dma16_lds(vt, vd[j], d + Dg::KB + j * 1024);
   };
+  auto load_slice = [&](int st, int i) { load_slice_at(st, k_at(i), v_at(i)); };
 
   // ---- query tile: chunk u of this wave's QI loads = column u / CH, chunk
   // (u % CH) ^ (column & (CH - 1)) at LDS k_off(column, chunk); a column past
@@ -1279,6 +1357,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   float mprev = kMinit, lprev = 0.0f;
   bool switched = false;
 
+  // paged cache: the page id of the next refill's tile (slice i + 2 in step
+  // i), read right after the previous refill, so that the scalar load lands
+  // while the step waits for its slice; the address is formed at the refill
+  auto slice_page = [&](int i) -> int32_t {
+    i = i < n_sl ? i : n_sl - 1;
+    return page_u(a.pm, s, (lo + 32 * (int64_t)i) / 64);
+  };
+  int32_t npg = 0;
+  if constexpr (PAGED) npg = slice_page(2);
   auto step = [&](int i, int st) {
     // slice i has landed; slice i + 1 (if any) stays in flight
     if (i + 1 < n_sl) wait_vmcnt<Dg::PER>();
@@ -1332,7 +1419,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
     if (i + 2 < n_sl) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       asm volatile("" ::: "memory");
-      load_slice(st, i + 2);
+      if constexpr (PAGED) {
+        const int64_t row = lo + 32 * (int64_t)(i + 2);
+        const int64_t tb = ((int64_t)npg * a.Hkv + kvh) * (64 * D) * 2;
+        load_slice_at(st, Kc + tb + (row % 64) * Dg::RB, Vc + tb + (row % 64) * 2);
+        npg = slice_page(i + 3);
+      } else {
+        load_slice(st, i + 2);
+      }
     }
   };
   for (int i = 0; i < n_sl; i += 2) {
@@ -1396,10 +1490,12 @@ struct F32Args {
   int32_t per_block, n_split, n_blocks;
   int32_t Hq, Hkv, G;
   float scale;
+  PageMap pm;  // phase 2 on a paged cache
 };
 
-template <int D, bool PHASE1>
+template <int D, bool PHASE1, bool PAGED>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
+  static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
   constexpr int E = D / 64;  // output dimensions per lane
   __shared__ float qsm[4][D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1432,8 +1528,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
   }
   const int64_t kvh = h / a.G;
   const int64_t head_row0 = (s * a.Hkv + kvh) * a.rows;
-  const float* K = a.k + head_row0 * D;
-  const float* V = a.v + head_row0 * D;
+  const float* K = PAGED ? a.k : a.k + head_row0 * D;
+  const float* V = PAGED ? a.v : a.v + head_row0 * D;
+  // element offset of this (sequence, kv head)'s tile t from K and from V
+  auto tile_at = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, (int)s, (int)kvh, t);
+    else return t * 64 * D;
+  };
   const float* qp = a.q + ((s * a.q_tokens + r) * a.Hq + h) * D;
   for (int e = lane; e < D; e += 64) qsm[w][e] = qp[e];
   __builtin_amdgcn_wave_barrier();
@@ -1449,8 +1550,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
       const bool ok = key < hi;
       float sc = -INFINITY;
       if (ok) {
+        const float* kp = K + tile_at(key / 64) + (key % 64) * D;
         float dot = 0.0f;
-        for (int e = 0; e < D; ++e) dot = fmaf(qsm[w][e], K[key * D + e], dot);
+        for (int e = 0; e < D; ++e) dot = fmaf(qsm[w][e], kp[e], dot);
         sc = dot * a.scale;
       }
       const float m_new = fmaxf(m, wave_max(sc));
@@ -1464,7 +1566,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
       for (int kk = 0; kk < cnt; ++kk) {
         const float pk = __shfl(p, kk, 64);
         const int64_t kr = base + kk;
-        const float* vt = V + (kr / 64) * 64 * D + (kr % 64);
+        const float* vt = V + tile_at(kr / 64) + (kr % 64);
 #pragma unroll
         for (int j = 0; j < E; ++j) o[j] = fmaf(pk, vt[(lane + 64 * j) * 64], o[j]);
       }
@@ -1591,9 +1693,11 @@ constexpr int kWideWaves = 8;
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
-                    const void* vs, int64_t n_tok, void* stream) {
+template <bool PAGED>
+static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
+                         const void* vs, int64_t n_tok, const PageMap& pm, void* stream) {
   KvArgs a;
+  a.pm = pm;
   a.kc = kc;
   a.vc = vc;
   a.ks = ks;
@@ -1607,13 +1711,25 @@ int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void*
   const dim3 grid((unsigned)((int64_t)a.nt * d.B * d.Hkv));
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == STAR_BF16) {
-    if (d.D == 128) hipLaunchKernelGGL((kv_write_kernel<uint16_t, 128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((kv_write_kernel<uint16_t, 64>), grid, dim3(256), 0, st, a);
+    if (d.D == 128)
+      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 128, PAGED>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 64, PAGED>), grid, dim3(256), 0, st, a);
   } else {
-    if (d.D == 128) hipLaunchKernelGGL((kv_write_kernel<float, 128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((kv_write_kernel<float, 64>), grid, dim3(256), 0, st, a);
+    if (d.D == 128)
+      hipLaunchKernelGGL((kv_write_kernel<float, 128, PAGED>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((kv_write_kernel<float, 64, PAGED>), grid, dim3(256), 0, st, a);
   }
   return check_launch();
+}
+
+int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
+                    const void* vs, int64_t n_tok, void* stream, const int32_t* table,
+                    int32_t maxp) {
+  const PageMap pm{table, maxp};
+  return table ? kv_write_impl<true>(d, kc, vc, pos0, ks, vs, n_tok, pm, stream)
+               : kv_write_impl<false>(d, kc, vc, pos0, ks, vs, n_tok, pm, stream);
 }
 
 static F32Args f32_args(const Dims& d, const void* kc, const void* vc, const void* q) {
@@ -1642,8 +1758,8 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
     a.q_tokens = d.L;
     a.n_cols = (int64_t)d.B * d.L * d.Hq;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, dim3(256), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, true, false>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -1670,10 +1786,10 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
   const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
   const dim3 grid((unsigned)nwg);
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true, false>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
@@ -1707,19 +1823,23 @@ static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, cons
   return a;
 }
 
-template <bool FUSED>
+template <bool FUSED, bool PAGED>
 static void launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.NG * a.WPG));
-  if (d.D == 128) hipLaunchKernelGGL((attn_decode_kernel<128, FUSED>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_decode_kernel<64, FUSED>), grid, dim3(256), 0, st, a);
+  if (d.D == 128)
+    hipLaunchKernelGGL((attn_decode_kernel<128, FUSED, PAGED>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<64, FUSED, PAGED>), grid, dim3(256), 0, st, a);
 }
 
-int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
-                          int64_t kv_len, const void* q, int64_t n_query, float* o_part,
-                          float* lse_part, void* stream) {
+template <bool PAGED>
+static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, const void* vc,
+                               int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                               float* lse_part, const PageMap& pm, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == STAR_F32) {
     F32Args a = f32_args(d, kc, vc, q);
+    a.pm = pm;
     a.o_part = o_part;
     a.lse_part = lse_part;
     a.q_tokens = n_query;
@@ -1730,12 +1850,14 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     a.n_split = p.n_split;
     a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, dim3(256), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false, PAGED>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, false, PAGED>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   if (p.narrow && p.balanced) {
-    launch_decode<false>(d, decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part), st);
+    DecodeArgs a = decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part);
+    a.pm = pm;
+    launch_decode<false, PAGED>(d, a, st);
     return check_launch();
   }
   if (p.narrow) {
@@ -1761,9 +1883,12 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
     a.NG = d.B * d.Hkv;
     a.scale = d.scale;
     a.c2 = d.scale_log2;
+    a.pm = pm;
     const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
-    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_narrow_kernel<64, false>), grid, dim3(256), 0, st, a);
+    if (d.D == 128)
+      hipLaunchKernelGGL((attn_narrow_kernel<128, false, PAGED>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_narrow_kernel<64, false, PAGED>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -1793,26 +1918,38 @@ int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const vo
   a.NRT = p.n_qtiles;
   a.scale = d.scale;
   a.c2 = d.scale_log2;
+  a.pm = pm;
   const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
 
-int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
-                       const void* q, const void* k_new, const void* v_new, int64_t n_query,
-                       float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
-                       void* stream) {
+int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
+                          int64_t kv_len, const void* q, int64_t n_query, float* o_part,
+                          float* lse_part, void* stream, const int32_t* table, int32_t maxp) {
+  const PageMap pm{table, maxp};
+  return table ? phase2_partial_impl<true>(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part, pm,
+                                           stream)
+               : phase2_partial_impl<false>(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part, pm,
+                                            stream);
+}
+
+template <bool PAGED>
+static int decode_step_impl(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
+                            const void* q, const void* k_new, const void* v_new, int64_t n_query,
+                            float* o_part, float* lse_part, const PageMap& pm, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (p.balanced) {
     DecodeArgs a = decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part);
     a.k_new = (const uint16_t*)k_new;
     a.v_new = (const uint16_t*)v_new;
-    launch_decode<true>(d, a, st);
+    a.pm = pm;
+    launch_decode<true, PAGED>(d, a, st);
   } else {
     NarrowArgs a{};
     a.k = (const uint16_t*)kc;
@@ -1838,11 +1975,25 @@ int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t
     a.c2 = d.scale_log2;
     a.k_new = (const uint16_t*)k_new;
     a.v_new = (const uint16_t*)v_new;
+    a.pm = pm;
     const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
-    if (d.D == 128) hipLaunchKernelGGL((attn_narrow_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_narrow_kernel<64, true>), grid, dim3(256), 0, st, a);
+    if (d.D == 128)
+      hipLaunchKernelGGL((attn_narrow_kernel<128, true, PAGED>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_narrow_kernel<64, true, PAGED>), grid, dim3(256), 0, st, a);
   }
-  const int rc = check_launch();
+  return check_launch();
+}
+
+int launch_decode_step(const Dims& d, const Plan& p, void* kc, void* vc, int64_t kv_len,
+                       const void* q, const void* k_new, const void* v_new, int64_t n_query,
+                       float* o_part, float* lse_part, void* o, int32_t o_dtype, float* lse_out,
+                       void* stream, const int32_t* table, int32_t maxp) {
+  const PageMap pm{table, maxp};
+  const int rc = table ? decode_step_impl<true>(d, p, kc, vc, kv_len, q, k_new, v_new, n_query,
+                                                o_part, lse_part, pm, stream)
+                       : decode_step_impl<false>(d, p, kc, vc, kv_len, q, k_new, v_new, n_query,
+                                                 o_part, lse_part, pm, stream);
   if (rc) return rc;
   return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }

@@ -83,25 +83,36 @@ class Pipeline:
             self._ws[key] = (n_split, o_part, lse_part, o, lse)
         return self._ws[key]
 
-    def attend(self, kv_len, q, n_query):
-        n_split, o_part, lse_part, o, lse = self.workspace(kv_len, n_query)
+    # the phase-2 calls on the cache (the paged pipeline overrides these three)
+    def kv_write2(self, pos0, k, v, n_tok):
+        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, pos0, k, v, n_tok)
+
+    def partial2(self, kv_len, q, n_query, o_part, lse_part):
         sa.star_attn_phase2_partial(self.desc, self.k_cache, self.v_cache, kv_len, q, n_query,
                                     o_part, lse_part)
+
+    def decode_call(self, kv_len, row, o_part, lse_part, o, lse):
+        """star_attn_decode_step for tail row ``row`` at kv_len."""
+        sa.star_attn_decode_step(self.desc, self.k_cache, self.v_cache, kv_len,
+                                 self.q_tail_rows[row], self.k_tail_rows[row],
+                                 self.v_tail_rows[row], 1, o_part, lse_part, o, self.dtype, lse)
+
+    def attend(self, kv_len, q, n_query):
+        n_split, o_part, lse_part, o, lse = self.workspace(kv_len, n_query)
+        self.partial2(kv_len, q, n_query, o_part, lse_part)
         sa.star_attn_lse_merge(self.desc, n_query, n_split, o_part, lse_part, o, self.dtype, lse)
         return o, lse
 
     def query_step(self):
         w = self.w
-        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, w.ctx_len, self.k_query,
-                         self.v_query, w.n_query)
+        self.kv_write2(w.ctx_len, self.k_query, self.v_query, w.n_query)
         return self.attend(w.ctx_len + w.n_query, self.q_query, w.n_query)
 
     def decode_step(self, t):
         """Decode step t (0-based): append tail row n_query + t, attend with it."""
         w = self.w
         row = w.n_query + t
-        sa.star_kv_write(self.desc, self.k_cache, self.v_cache, w.ctx_len + row,
-                         self.k_tail_rows[row], self.v_tail_rows[row], 1)
+        self.kv_write2(w.ctx_len + row, self.k_tail_rows[row], self.v_tail_rows[row], 1)
         return self.attend(w.ctx_len + row + 1, self.q_tail_rows[row], 1)
 
     def decode_step_fused(self, t):
@@ -110,9 +121,7 @@ class Pipeline:
         row = w.n_query + t
         kv_len = w.ctx_len + row + 1
         n_split, o_part, lse_part, o, lse = self.workspace(kv_len, 1)
-        sa.star_attn_decode_step(self.desc, self.k_cache, self.v_cache, kv_len,
-                                 self.q_tail_rows[row], self.k_tail_rows[row],
-                                 self.v_tail_rows[row], 1, o_part, lse_part, o, self.dtype, lse)
+        self.decode_call(kv_len, row, o_part, lse_part, o, lse)
         return o, lse
 
     def run_tail(self, fused=False):
@@ -125,3 +134,45 @@ class Pipeline:
             outs.append(to_host_f64(o))
             lses.append(lse.cpu().numpy().astype(np.float64))
         return np.concatenate(outs, axis=1), np.concatenate(lses, axis=1)
+
+
+class PagedPipeline(Pipeline):
+    """The same workload with phase 2 on a paged cache: page pools with
+    ``spare`` extra pages, a block table that is a seeded random permutation
+    of the pages, unused pages NaN-filled (a stray read shows up). Phase 1
+    reads the contiguous cache, which ``write_context`` fills as well."""
+
+    def __init__(self, w: syn.Workload, inputs=None, device="cuda", fill_nan=True, threads=None,
+                 spare=5, table_seed=7):
+        super().__init__(w, inputs=inputs, device=device, fill_nan=fill_nan, threads=threads)
+        self.maxp = -(-(w.ctx_len + w.tail_cap) // sa.binding.STAR_KV_TILE)
+        self.n_pages = w.batch * self.maxp + spare
+        self.k_pages = sa.alloc_kv_pages(self.desc, self.n_pages, device)
+        self.v_pages = sa.alloc_kv_pages(self.desc, self.n_pages, device)
+        for c in (self.k_pages, self.v_pages):
+            if w.dtype == "bf16":
+                c.view(torch.int16).fill_(NAN_BF16)
+            else:
+                c.fill_(float("nan"))
+        perm = np.random.default_rng(table_seed).permutation(self.n_pages)[: w.batch * self.maxp]
+        self.table_host = perm.reshape(w.batch, self.maxp).astype(np.int32)
+        self.table = torch.from_numpy(self.table_host).to(device)
+
+    def write_context(self):
+        super().write_context()
+        w = self.w
+        sa.star_kv_write_paged(self.desc, self.k_pages, self.v_pages, self.table, 0,
+                               self.dev["k_ctx"], self.dev["v_ctx"], w.ctx_len)
+
+    def kv_write2(self, pos0, k, v, n_tok):
+        sa.star_kv_write_paged(self.desc, self.k_pages, self.v_pages, self.table, pos0, k, v, n_tok)
+
+    def partial2(self, kv_len, q, n_query, o_part, lse_part):
+        sa.star_attn_phase2_partial_paged(self.desc, self.k_pages, self.v_pages, self.table,
+                                          kv_len, q, n_query, o_part, lse_part)
+
+    def decode_call(self, kv_len, row, o_part, lse_part, o, lse):
+        sa.star_attn_decode_step_paged(self.desc, self.k_pages, self.v_pages, self.table, kv_len,
+                                       self.q_tail_rows[row], self.k_tail_rows[row],
+                                       self.v_tail_rows[row], 1, o_part, lse_part, o, self.dtype,
+                                       lse)

@@ -218,3 +218,41 @@ def test_decode_plan_is_balanced_at_128k(kv_len):
     assert max(lens) <= r
     assert n <= 128 + 9          # 128 ranges, at most one extra split per host boundary
     assert sum(lens) == kv_len
+
+
+def test_paged_entry_points_validate_before_launching():
+    """Paged calls: page size, and every argument check (null pools or table,
+    a table too short for the cache's capacity, the contiguous calls' shape
+    checks) fails before any device memory is touched."""
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc()  # ctx 131072 + tail 320, Hkv 8, d 128, bf16
+    assert sa.star_kv_page_bytes(d) == 8 * 64 * 128 * 2
+    f32 = _desc(dtype=B.STAR_F32, head_dim=64)
+    assert sa.star_kv_page_bytes(f32) == 8 * 64 * 64 * 4
+    dp = ctypes.byref(d)
+    need = -(-(131072 + 320) // 64)
+    E, S = B.STAR_ERR_INVALID_ARG, B.STAR_ERR_SHAPE
+    # null pools / table
+    assert lib.star_kv_write_paged(dp, None, fake, fake, need, 0, fake, fake, 1, None) == E
+    assert lib.star_kv_write_paged(dp, fake, fake, None, need, 0, fake, fake, 1, None) == E
+    assert lib.star_attn_phase2_partial_paged(dp, fake, None, fake, need, 131073, fake, 1, fake,
+                                              fake, None) == E
+    assert lib.star_attn_decode_step_paged(dp, fake, fake, None, need, 131073, fake, fake, fake, 1,
+                                           fake, fake, fake, 0, None, None) == E
+    # a table shorter than the capacity
+    assert lib.star_kv_write_paged(dp, fake, fake, fake, need - 1, 0, fake, fake, 1, None) == S
+    assert lib.star_attn_phase2_partial_paged(dp, fake, fake, fake, need - 1, 131073, fake, 1,
+                                              fake, fake, None) == S
+    assert lib.star_attn_decode_step_paged(dp, fake, fake, fake, need - 1, 131073, fake, fake,
+                                           fake, 1, fake, fake, fake, 0, None, None) == S
+    # the contiguous calls' checks still apply
+    assert lib.star_kv_write_paged(dp, fake, fake, fake, need, 131072 + 320, fake, fake, 1,
+                                   None) == S
+    assert lib.star_attn_phase2_partial_paged(dp, fake, fake, fake, need, 131072, fake, 1, fake,
+                                              fake, None) == S
+    assert lib.star_attn_decode_step_paged(dp, fake, fake, fake, need, 131073, fake, fake, fake, 1,
+                                           fake, fake, fake, 7, None, None) == B.STAR_ERR_DTYPE
+    bad = ctypes.byref(_desc(n_kv_heads=3))
+    assert lib.star_kv_page_bytes(bad) == 0
+    assert lib.star_kv_write_paged(bad, fake, fake, fake, need, 0, fake, fake, 1, None) == S

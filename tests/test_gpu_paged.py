@@ -1,0 +1,123 @@
+"""GPU parity of phase 2 on the paged cache (block table).
+
+The paged calls differ from the contiguous-cache calls only in where a tile
+is read or written, so their outputs must be bit-identical on the same
+inputs; they are also checked against the fp64 oracle. The page pools hold
+spare NaN-filled pages and the block table is a random permutation of the
+pages, so a wrong page, or a read of a row nobody wrote, shows up. The
+layout that star_kv_write_paged produces is checked element by element
+against its definition in star_attn.h.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_phase1_amd as sa
+from long_context_attention_phase1_amd import synthetic as syn
+from oracle import star_oracle as orc
+from tests.gpu_pipeline import PagedPipeline, Pipeline, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+TOL_LSE = {"bf16": 2e-3, "f32": 1e-5}
+
+W = syn.Workload
+CASES = {
+    # balanced decode plan (per-wave kernel), host boundaries inside ranges
+    "balanced_bnd": W("balanced_bnd", 1, 8, 2, 128, 2176, 1088, 512, 4, 3, "bf16", seed=15),
+    "balanced_b2_g8_d64": W("bal_b2", 2, 16, 2, 64, 1536, 448, 200, 3, 2, "bf16", seed=16),
+    # blockwise plan (narrow kernel): unaligned blocks, ragged last block
+    "g1_unaligned_a_lt_b": W("g1_unaligned", 2, 4, 4, 128, 333, 100, 37, 5, 2, "bf16", seed=2),
+    "gqa4_d128_ragged": W("gqa4_d128_ragged", 1, 8, 2, 128, 640, 256, 256, 8, 3, "bf16", seed=1),
+    # > 32 query columns (wide kernel) with an empty split
+    "long_tail_wide": W("long_tail", 1, 4, 2, 128, 128, 64, 64, 300, 1, "bf16", seed=13),
+    "g4_d64_many_blocks": W("g4_d64", 1, 8, 2, 64, 1024, 128, 128, 40, 1, "bf16", seed=8),
+    # fp32 path
+    "tiny_f32": syn.WORKLOADS["tiny_f32"],
+    "f32_gqa_d128": W("f32_gqa", 1, 4, 2, 128, 130, 64, 10, 3, 2, "f32", seed=7),
+}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+
+
+def test_kv_write_paged_layout_bit_exact():
+    _need_gpu()
+    for dtype, d in (("bf16", 128), ("bf16", 64), ("f32", 64)):
+        w = W("layout", 2, 6, 3, d, 150, 64, 64, 9, 0, dtype, seed=9)
+        p = PagedPipeline(w, threads=1, spare=3, table_seed=11)
+        p.write_context()
+        # tail rows in two unaligned pieces
+        p.kv_write2(w.ctx_len, p.k_query[:, :4].contiguous(), p.v_query[:, :4].contiguous(), 4)
+        p.kv_write2(w.ctx_len + 5, p.k_query[:, 5:9].contiguous(), p.v_query[:, 5:9].contiguous(), 4)
+        torch.cuda.synchronize()
+        raw = np.uint16 if dtype == "bf16" else np.uint32
+        iv = torch.int16 if dtype == "bf16" else torch.int32
+        kp = p.k_pages.view(iv).cpu().numpy().view(raw).reshape(p.n_pages, w.n_kv_heads, 64, d)
+        vp = p.v_pages.view(iv).cpu().numpy().view(raw).reshape(p.n_pages, w.n_kv_heads, d, 64)
+        k_rows = np.concatenate([p.inputs["k_ctx"], p.inputs["k_tail"][:, :9]], axis=1).view(raw)
+        v_rows = np.concatenate([p.inputs["v_ctx"], p.inputs["v_tail"][:, :9]], axis=1).view(raw)
+        nan = 0x7FC0 if dtype == "bf16" else np.float32(np.nan).view(np.uint32)
+        used = set(p.table_host.ravel().tolist())
+        for page in range(p.n_pages):
+            if page not in used:  # spare pages are never written
+                assert np.all(kp[page] == nan) and np.all(vp[page] == nan), (dtype, page)
+        for s in range(w.batch):
+            for r in range(p.maxp * 64):
+                page = p.table_host[s, r // 64]
+                written = r < w.ctx_len + 4 or (w.ctx_len + 5 <= r < w.ctx_len + 9)
+                for g in range(w.n_kv_heads):
+                    kr, vr = kp[page, g, r % 64], vp[page, g, :, r % 64]
+                    if written:
+                        assert np.array_equal(kr, k_rows[s, r, g]), (dtype, d, s, r, g)
+                        assert np.array_equal(vr, v_rows[s, r, g]), (dtype, d, s, r, g)
+                    else:
+                        assert np.all(kr == nan) and np.all(vr == nan), (dtype, d, s, r, g)
+
+
+def _tail_both(w, fused, threads=4):
+    p0 = Pipeline(w, threads=threads)
+    p1 = PagedPipeline(w, inputs=p0.inputs, threads=threads)
+    p0.write_context()
+    p1.write_context()
+    a = p0.run_tail(fused=fused)
+    b = p1.run_tail(fused=fused)
+    torch.cuda.synchronize()
+    return p0, a, b
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "separate_calls"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_paged_phase2_bit_identical_to_contiguous(name, fused):
+    _need_gpu()
+    w = CASES[name]
+    p0, (o0, l0), (o1, l1) = _tail_both(w, fused)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1), \
+        (name, float(np.abs(o0 - o1).max()), float(np.abs(l0 - l1).max()))
+    x = {k: syn.to_f64(v, w.dtype) for k, v in p0.inputs.items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    ref_o, ref_l = orc.decode_loop(x["q_tail"], x["k_ctx"], x["v_ctx"], x["k_tail"], x["v_tail"],
+                                   w.n_query, sc)
+    eo, el = float(np.abs(o1 - ref_o).max()), float(np.abs(l1 - ref_l).max())
+    print(f"{name}: paged == contiguous; vs oracle o {eo:.3e}, lse {el:.3e}")
+    assert eo <= TOL[w.dtype] and el <= TOL_LSE[w.dtype]
+
+
+@pytest.mark.timeout(600)
+def test_paged_full_size_128k_bit_identical():
+    """The 128K workload's query step and all 256 decode steps, as the bench
+    runs them, on the paged cache: bit-identical to the contiguous cache."""
+    _need_gpu()
+    w = syn.workload("llama8b_128k_peaked")
+    p0 = Pipeline(w, threads=16, fill_nan=False)
+    p1 = PagedPipeline(w, inputs=p0.inputs, fill_nan=False)
+    p0.write_context()
+    p1.write_context()
+    o0, l0 = p0.run_tail(fused=True)
+    o1, l1 = p1.run_tail(fused=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    assert np.isfinite(o1).all() and np.isfinite(l1).all()
