@@ -101,6 +101,16 @@ SWEEPS: Dict[str, Workload] = {
 }
 
 
+def rope_tables(head_dim: int, n_pos: int, theta: float = 500000.0):
+    """Rotary-embedding tables of a model (input data, like its weights):
+    float32 ``cos``, ``sin`` of shape ``[n_pos, head_dim / 2]`` with angle
+    ``pos * theta ** (-2 i / head_dim)``, computed in float64. The default
+    base is the Llama-3 models' one."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * theta ** (-2.0 * i / head_dim)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def workload(name: str) -> Workload:
     """A workload of the scope table or a sweep variant, by name."""
     if name in WORKLOADS:

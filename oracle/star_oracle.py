@@ -390,3 +390,99 @@ def brute_force_phase2(q_rows, k_all, v_all, positions, scale):
         O.append(orow)
         LSE.append(lrow)
     return O, LSE
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding in phase 1: the anchor's position ids
+# --------------------------------------------------------------------------
+#
+# paperhub.cn rebuttal, reply to reviewer x5MA point 1: with the first block
+# as the anchor, the position ids given to the anchor tokens during the local
+# attention of phase 1 change the result little. The pages name no
+# positional scheme and give no formula. Readings:
+#   * rotary position embedding (RoFormer), the scheme of the Llama models
+#     the pages evaluate, with half-split pairing: element i of a head vector
+#     is rotated together with element i + d/2 (i < d/2) by the angle whose
+#     cosine and sine are entry [pos][i] of caller-given tables;
+#   * two anchor modes for a row of block i >= 1:
+#       ORIGINAL - anchor row j keeps position j (its place in the context);
+#       ADJACENT - anchor row j takes position i*b - a + j, directly before
+#                  the block, as if the anchor had been prepended to it;
+#     every other key and every query keeps its context position.
+ROPE_ORIGINAL, ROPE_ADJACENT = 0, 1
+
+
+def rope_rotate(x: np.ndarray, cos_rows: np.ndarray, sin_rows: np.ndarray) -> np.ndarray:
+    """Rotate head vectors ``x[..., d]`` by the table rows ``cos_rows[..., d/2]``,
+    ``sin_rows[..., d/2]`` (one row per vector), in float64:
+    ``y_i = x_i c_i - x_{i+d/2} s_i``, ``y_{i+d/2} = x_{i+d/2} c_i + x_i s_i``."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    c = np.asarray(cos_rows, dtype=np.float64)
+    s = np.asarray(sin_rows, dtype=np.float64)
+    lo, hi = x[..., :h], x[..., h:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def _round_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> the nearest bfloat16 (ties to even), returned as float32."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def rope_rotate_bf16(x: np.ndarray, cos_rows: np.ndarray, sin_rows: np.ndarray) -> np.ndarray:
+    """The rotation as a bf16 model stores its rotated keys: every product and
+    the sum or difference rounded to float32 (no fused multiply-add), then the
+    result rounded to bfloat16. Returns float64 values."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.shape[-1] // 2
+    c = np.asarray(cos_rows, dtype=np.float32)
+    s = np.asarray(sin_rows, dtype=np.float32)
+    lo, hi = x[..., :h], x[..., h:]
+    y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)
+    return _round_bf16(y).astype(np.float64)
+
+
+def phase1_rope_positions(block_len: int, anchor_len: int, i: int, mode: int) -> np.ndarray:
+    """Position ids of the anchor rows ``[0, a)`` as block ``i >= 1`` sees them."""
+    j = np.arange(anchor_len, dtype=np.int64)
+    return j if mode == ROPE_ORIGINAL else i * block_len - anchor_len + j
+
+
+def phase1_rope(q_ctx: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, block_len: int,
+                anchor_len: int, scale: float, cos_tab: np.ndarray, sin_tab: np.ndarray,
+                mode: int) -> np.ndarray:
+    """Phase 1 with rotary position embedding: ``q_ctx`` and ``k_ctx`` hold the
+    un-rotated head vectors ``[B, L, H, d]``; every query and key is rotated
+    at its position id (context position; anchor rows per ``mode``) before
+    the same blockwise-local causal attention as ``phase1``. float64, exact
+    rotations."""
+    B, L, Hq, d = q_ctx.shape
+    Hkv = k_ctx.shape[2]
+    out = np.zeros((B, L, Hq, d), dtype=np.float64)
+    n_blocks = -(-L // block_len)
+    ctx_pos = np.arange(L, dtype=np.int64)
+    for s in range(B):
+        for i in range(n_blocks):
+            lo, hi = i * block_len, min((i + 1) * block_len, L)
+            n_loc = hi - lo
+            if i > 0:
+                anc_rows = np.arange(anchor_len, dtype=np.int64)
+                anc_pos = phase1_rope_positions(block_len, anchor_len, i, mode)
+            else:
+                anc_rows = anc_pos = np.arange(0, dtype=np.int64)
+            rows = np.concatenate([anc_rows, np.arange(lo, hi)])
+            pos = np.concatenate([anc_pos, ctx_pos[lo:hi]])
+            visible = np.zeros((n_loc, rows.size), dtype=bool)
+            visible[:, :anc_rows.size] = True
+            visible[:, anc_rows.size:] = np.tri(n_loc, dtype=bool)  # causal, diagonal included
+            for h in range(Hq):
+                g = kv_head(h, Hq, Hkv)
+                Q = rope_rotate(q_ctx[s, lo:hi, h], cos_tab[lo:hi], sin_tab[lo:hi])
+                K = rope_rotate(k_ctx[s, rows, g], cos_tab[pos], sin_tab[pos])
+                V = v_ctx[s, rows, g]
+                S = np.where(visible, (Q @ K.T) * scale, -np.inf)
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                out[s, lo:hi, h] = (E @ V) / np.sum(E, axis=1, keepdims=True)
+    return out

@@ -337,4 +337,146 @@ def pin_sampled_row_forms_match_sdpa(orc):
         _close(l, lref[0, :, g * 3:(g + 1) * 3], what=f"sampled phase2 lse g={g}")
 
 
+# ------------------------------------------------------------------ rotary embedding
+
+def _angles(n_pos, d, theta=10000.0, offset=0):
+    """Angle table ``[n_pos, d/2]``: (offset + pos) * theta^(-2i/d)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return (offset + np.arange(n_pos, dtype=np.float64))[:, None] * theta ** (-2.0 * i / d)
+
+
+def _rot_complex(x, ang):
+    """Half-split rotation written as complex multiplication: element i and
+    element i + d/2 are the real and imaginary parts of one number, turned by
+    the angle."""
+    h = x.shape[-1] // 2
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def pin_rope_is_complex_multiplication(orc):
+    x = _rng(40).standard_normal((7, 16))
+    ang = _angles(7, 16) * 3.1
+    _close(orc.rope_rotate(x, np.cos(ang), np.sin(ang)), _rot_complex(x, ang), 1e-12, "rope")
+
+
+def pin_rope_scores_depend_on_relative_position(orc):
+    """<R(p) q, R(p') k> depends only on p - p' (tables from true angles)."""
+    r = _rng(41)
+    q, k = r.standard_normal(16), r.standard_normal(16)
+    a0, a1 = _angles(64, 16), _angles(64, 16, offset=1000)
+    for p, pk in ((9, 2), (40, 40), (3, 50)):
+        s0 = orc.rope_rotate(q, np.cos(a0[p]), np.sin(a0[p])) @ \
+            orc.rope_rotate(k, np.cos(a0[pk]), np.sin(a0[pk]))
+        s1 = orc.rope_rotate(q, np.cos(a1[p]), np.sin(a1[p])) @ \
+            orc.rope_rotate(k, np.cos(a1[pk]), np.sin(a1[pk]))
+        _close(s0, s1, 1e-9, "relative position")
+
+
+def pin_rope_bf16_is_torch_fp32_then_bf16(orc):
+    """The bf16 form equals torch's float32 arithmetic (separate multiply and
+    add on the CPU) followed by torch's bfloat16 conversion (nearest, ties to
+    even), on bf16 inputs, including values on rounding ties."""
+    r = _rng(42)
+    x = torch.from_numpy(r.standard_normal((33, 32)).astype(np.float32)).to(torch.bfloat16).float()
+    ang = _angles(33, 32, theta=500000.0) * 1.7
+    c = torch.from_numpy(np.cos(ang).astype(np.float32))
+    sn = torch.from_numpy(np.sin(ang).astype(np.float32))
+    lo, hi = x[:, :16], x[:, 16:]
+    y = torch.cat([lo * c - hi * sn, hi * c + lo * sn], dim=1).to(torch.bfloat16).double()
+    _close(orc.rope_rotate_bf16(x.numpy(), c.numpy(), sn.numpy()), y.numpy(), 0.0, "rope bf16")
+    # cancellation: rounding each product to float32 gives 2^-23, the exact
+    # difference 2^-23 (1 + 2^-7); both are bf16 values
+    xc = torch.tensor([[1.0078125, 1.0078125]], dtype=torch.float32)
+    cc = torch.tensor([[1.0 + 3 * 2.0 ** -23]], dtype=torch.float32)
+    sc_ = torch.tensor([[1.0 + 2.0 ** -22]], dtype=torch.float32)
+    yc = (xc[:, :1] * cc - xc[:, 1:] * sc_).to(torch.bfloat16).double()
+    assert float(yc) == 2.0 ** -23
+    _close(orc.rope_rotate_bf16(xc.numpy(), cc.numpy(), sc_.numpy())[:, :1], yc.numpy(), 0.0,
+           "cancellation")
+    # exact ties: 1 + 2^-8 (tie, even below) and 1 + 3 * 2^-8 (tie, even above)
+    t = np.array([[1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 0.0, 0.0]], dtype=np.float32)
+    one, zero = np.ones((1, 2), np.float32), np.zeros((1, 2), np.float32)
+    _close(orc.rope_rotate_bf16(t, one, zero)[0, :2], [1.0, 1.0 + 2.0 ** -6], 0.0, "ties")
+
+
+def _rope_case(seed, L=21, b=8, a=5, Hq=4, Hkv=2, d=8):
+    q, k, v = _qkv(seed, 2, L, Hq, Hkv, d)
+    ang = _angles(L, d) * 0.9
+    return q, k, v, b, a, ang
+
+
+def pin_phase1_rope_identity_table_is_phase1(orc):
+    q, k, v, b, a, ang = _rope_case(43)
+    L, h = q.shape[1], q.shape[3] // 2
+    one, zero = np.ones((L, h)), np.zeros((L, h))
+    sc = _scale(orc, q.shape[3])
+    for mode in (orc.ROPE_ORIGINAL, orc.ROPE_ADJACENT):
+        _close(orc.phase1_rope(q, k, v, b, a, sc, one, zero, mode),
+               orc.phase1(q, k, v, b, a, sc), 1e-12, f"identity table, mode {mode}")
+
+
+def pin_phase1_rope_original_is_phase1_of_rotated_inputs(orc):
+    """ORIGINAL: every row keeps its context position, so the result is plain
+    phase 1 on inputs rotated beforehand (by the complex form)."""
+    q, k, v, b, a, ang = _rope_case(44)
+    sc = _scale(orc, q.shape[3])
+    qr = _rot_complex(q, ang[None, :, None, :])
+    kr = _rot_complex(k, ang[None, :, None, :])
+    _close(orc.phase1_rope(q, k, v, b, a, sc, np.cos(ang), np.sin(ang), orc.ROPE_ORIGINAL),
+           orc.phase1(qr, kr, v, b, a, sc), 1e-12, "original")
+
+
+def pin_phase1_rope_adjacent_brute_force(orc):
+    """ADJACENT, row by row from the stated position ids: anchor row j of
+    block i >= 1 at position i*b - a + j, every other row at its own, each
+    query attending to the anchor then causally to its block."""
+    q, k, v, b, a, ang = _rope_case(45)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sc = _scale(orc, d)
+    ext = _angles(2 * L, d) * 0.9  # the same schedule, positions up to 2L
+    got = orc.phase1_rope(q, k, v, b, a, sc, np.cos(ext), np.sin(ext), orc.ROPE_ADJACENT)
+    for s in range(B):
+        for r in range(L):
+            i = r // b
+            keys = list(range(i * b, r + 1))
+            pos = list(keys)
+            if i > 0:
+                keys = list(range(a)) + keys
+                pos = [i * b - a + j for j in range(a)] + pos
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                qq = _rot_complex(q[s, r, h], ext[r])
+                kk = np.stack([_rot_complex(k[s, kr, g], ext[p]) for kr, p in zip(keys, pos)])
+                w = np.exp(sc * (kk @ qq) - np.max(sc * (kk @ qq)))
+                _close(got[s, r, h], (w @ v[s, keys, g]) / w.sum(), 1e-12, f"row {r}")
+
+
+def pin_phase1_rope_adjacent_is_query_shift(orc):
+    """Rotations compose, so ADJACENT scores for block i equal those of keys
+    kept at their own positions with the query turned back by i*b - a for the
+    anchor part: the identity the kernel relies on, checked here on the
+    oracle against a run that applies it explicitly."""
+    q, k, v, b, a, ang = _rope_case(46, L=24, b=8, a=8)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sc = _scale(orc, d)
+    ext = _angles(2 * L, d) * 0.7
+    got = orc.phase1_rope(q, k, v, b, a, sc, np.cos(ext), np.sin(ext), orc.ROPE_ADJACENT)
+    for s in range(B):
+        for r in range(b, L):
+            i, delta = r // b, (r // b) * b - a
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                qa = _rot_complex(q[s, r, h], ext[r - delta])
+                ql = _rot_complex(q[s, r, h], ext[r])
+                ka = np.stack([_rot_complex(k[s, j, g], ext[j]) for j in range(a)])
+                kl = np.stack([_rot_complex(k[s, j, g], ext[j]) for j in range(i * b, r + 1)])
+                sco = sc * np.concatenate([ka @ qa, kl @ ql])
+                w = np.exp(sco - sco.max())
+                vv = np.concatenate([v[s, :a, g], v[s, i * b:r + 1, g]])
+                _close(got[s, r, h], (w @ vv) / w.sum(), 1e-12, f"shift row {r}")
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -108,6 +108,42 @@ MUTANTS = [
     ("sampled_softmax_unnormalised",
      "return (E @ V) / z, (m + np.log(z))[:, 0]",
      "return (E @ V), (m + np.log(z))[:, 0]"),
+    ("rope_sine_sign",
+     "return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)",
+     "return np.concatenate([lo * c + hi * s, hi * c - lo * s], axis=-1)"),
+    ("rope_pairs_neighbours",
+     "    lo, hi = x[..., :h], x[..., h:]\n    return np.concatenate([lo * c - hi * s",
+     "    lo, hi = x[..., 0::2], x[..., 1::2]\n    return np.concatenate([lo * c - hi * s"),
+    ("rope_bf16_rounds_half_up",
+     "u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16",
+     "u = (u + 0x8000) >> 16 << 16"),
+    ("rope_bf16_fused_in_float64",
+     "y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)",
+     "y = np.concatenate([(lo.astype(np.float64) * c) - (hi.astype(np.float64) * s), (hi.astype(np.float64) * c) + (lo.astype(np.float64) * s)], axis=-1).astype(np.float32)"),
+    ("rope_adjacent_no_anchor_shift",
+     "return j if mode == ROPE_ORIGINAL else i * block_len - anchor_len + j",
+     "return j if mode == ROPE_ORIGINAL else i * block_len + j"),
+    ("rope_adjacent_ignored",
+     "return j if mode == ROPE_ORIGINAL else i * block_len - anchor_len + j",
+     "return j"),
+    ("rope_query_not_rotated",
+     "Q = rope_rotate(q_ctx[s, lo:hi, h], cos_tab[lo:hi], sin_tab[lo:hi])",
+     "Q = q_ctx[s, lo:hi, h]"),
+    ("rope_keys_at_row_not_position",
+     "K = rope_rotate(k_ctx[s, rows, g], cos_tab[pos], sin_tab[pos])",
+     "K = rope_rotate(k_ctx[s, rows, g], cos_tab[rows], sin_tab[rows])"),
+    ("rope_phase1_sees_one_future_key",
+     "visible[:, anc_rows.size:] = np.tri(n_loc, dtype=bool)",
+     "visible[:, anc_rows.size:] = np.tri(n_loc, k=1, dtype=bool)"),
+    ("rope_phase1_missing_scale",
+     "S = np.where(visible, (Q @ K.T) * scale, -np.inf)",
+     "S = np.where(visible, (Q @ K.T), -np.inf)"),
+    ("rope_phase1_normalised_by_total",
+     "out[s, lo:hi, h] = (E @ V) / np.sum(E, axis=1, keepdims=True)",
+     "out[s, lo:hi, h] = (E @ V) / np.sum(E)"),
+    ("rope_phase1_anchor_on_block0",
+     "            if i > 0:\n                anc_rows = np.arange(anchor_len, dtype=np.int64)",
+     "            if i >= 0:\n                anc_rows = np.arange(anchor_len, dtype=np.int64)"),
 ]
 
 
