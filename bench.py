@@ -139,12 +139,17 @@ def main():
     ap.add_argument("--workload", default="llama8b_128k_peaked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=None)
+    ap.add_argument("--rope", choices=["none", "original", "adjacent"], default="none",
+                    help="phase 1 with the rotary embedding fused (K rotated by the context "
+                         "write, the query in phase 1), anchor position ids as named")
     ap.add_argument("--paged", action="store_true",
                     help="phase 2 (query step and decode loop) on a paged cache through a "
                          "block table; the context is written into the pages too")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
+    if args.paged and args.rope != "none":
+        ap.error("--paged writes the context unrotated into the pages: use it without --rope")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is measured on one GPU's share "
               f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
@@ -170,12 +175,21 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     p1_events, dec_bytes, q_events = [], [], []
+    rope = None
+    if args.rope != "none":
+        rope = p.rope(sa.STAR_ROPE_ADJACENT if args.rope == "adjacent" else sa.STAR_ROPE_ORIGINAL)
 
     def step(record: bool):
-        p.write_context()
+        if rope is None:
+            p.write_context()
+        else:
+            p.write_context_rope(rope)
         e0, e1 = ev(), ev()
         e0.record(stream)
-        p.phase1()
+        if rope is None:
+            p.phase1()
+        else:
+            p.phase1_rope(rope)
         e1.record(stream)
         if record:
             p1_events.append((e0, e1))
@@ -228,7 +242,8 @@ def main():
     step_us = dec_loop_ms * 1e3 / w.n_decode
 
     pg = "true" if args.paged else "false"
-    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false>"
+    rp = {"none": 0, "original": 1, "adjacent": 2}[args.rope]
+    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}>"
     kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}>", f"lse_merge_kernel<{w.head_dim}>")
     t1, t2 = load_traffic(kname1), load_traffic(*kname2)
     out = {
@@ -249,7 +264,8 @@ def main():
                    "block_len": w.block_len, "anchor_len": w.anchor_len,
                    "n_query": w.n_query, "n_decode": w.n_decode,
                    "peaked_k_rows": w.peak_frac, "peak_factor": w.peak_factor,
-                   "phase2_cache": "paged" if args.paged else "contiguous"},
+                   "phase2_cache": "paged" if args.paged else "contiguous",
+                   "rope": args.rope},
         "phase1_ms": p1_ms,
         "phase1_ctx_tokens_per_s": ctx_tok_s,
         "query_step_ms": q_ms,

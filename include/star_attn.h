@@ -249,6 +249,51 @@ int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void*
                                 int64_t n_query, float* o_part, float* lse_part, void* o,
                                 int32_t o_dtype, float* lse_out, void* stream);
 
+/*
+ * Rotary position embedding fused into phase 1, with the anchor's position
+ * ids (paperhub.cn rebuttal, reply to reviewer x5MA point 1: with the first
+ * block as the anchor, the position ids given to the anchor tokens in
+ * phase 1 change the result little). The pages name no scheme; this is the
+ * rotary embedding of the Llama models they evaluate, half-split pairing:
+ * element e < d/2 of a head vector turns together with element e + d/2,
+ *   y_e = x_e c - x_{e+d/2} s,   y_{e+d/2} = x_{e+d/2} c + x_e s,
+ * with (c, s) = (cos[pos][e], sin[pos][e]) from the caller's tables (any
+ * frequency schedule). Arithmetic is fp32, each product and sum rounded on
+ * its own; bf16 results are rounded once to nearest even (the rotated keys
+ * a bf16 model caches).
+ *   cos, sin     device fp32 tables [n_pos][head_dim / 2], 16-byte aligned
+ *   n_pos        rows of the tables; >= ctx_len + tail_cap (else
+ *                STAR_ERR_SHAPE)
+ *   anchor_mode  position ids of anchor row j (j < anchor_len) as block
+ *                i >= 1 sees it:
+ *                STAR_ROPE_ORIGINAL  j, its place in the context;
+ *                STAR_ROPE_ADJACENT  i*block_len - anchor_len + j, directly
+ *                                    before the block.
+ *                Every other key and every query keeps its context row.
+ */
+enum { STAR_ROPE_ORIGINAL = 0, STAR_ROPE_ADJACENT = 1 };
+
+typedef struct star_rope {
+  const float* cos;
+  const float* sin;
+  int64_t n_pos;
+  int32_t anchor_mode;
+} star_rope;
+
+/* star_kv_write with each K row rotated at its cache row pos0 + t (V is
+ * copied unchanged). The contiguous cache; same arguments and checks. */
+int star_kv_write_rope(const star_attn_desc* desc, void* k_cache, void* v_cache, int64_t pos0,
+                       const void* k_src, const void* v_src, int64_t n_tok,
+                       const star_rope* rope, void* stream);
+
+/* star_attn_phase1 with q_ctx not yet rotated: each query is rotated at its
+ * context row, and for the anchor pass of block i >= 1 at the row less
+ * (i*block_len - anchor_len) under STAR_ROPE_ADJACENT (rotations compose, so
+ * this equals keeping the query and giving the anchor rows the adjacent
+ * ids). The cache holds K rotated at its rows (star_kv_write_rope). */
+int star_attn_phase1_rope(const star_attn_desc* desc, const void* k_cache, const void* v_cache,
+                          const void* q_ctx, const star_rope* rope, void* o_ctx, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* star_attn_strerror(int status);
 

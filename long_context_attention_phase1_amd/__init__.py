@@ -10,4 +10,6 @@ from .binding import (STAR_BF16, STAR_F32, STAR_OK, StarAttnDesc, StarAttnError,
                       star_attn_lse_merge, star_attn_phase1, star_attn_phase2_partial,
                       star_attn_phase2_partial_paged, star_attn_phase2_plan,
                       star_attn_phase2_split_range, star_attn_strerror, star_kv_cache_bytes,
-                      star_kv_page_bytes, star_kv_write, star_kv_write_paged)
+                      star_kv_page_bytes, star_kv_write, star_kv_write_paged,
+                      STAR_ROPE_ADJACENT, STAR_ROPE_ORIGINAL, StarRope, make_rope,
+                      star_attn_phase1_rope, star_kv_write_rope)

@@ -32,8 +32,8 @@ STAR_KV_TILE = 64
 EXPORTS = ("star_kv_cache_bytes", "star_kv_write", "star_attn_phase1", "star_attn_phase2_plan",
            "star_attn_phase2_split_range", "star_attn_phase2_partial", "star_attn_lse_merge",
            "star_attn_decode_step", "star_kv_page_bytes", "star_kv_write_paged",
-           "star_attn_phase2_partial_paged", "star_attn_decode_step_paged", "star_attn_strerror",
-           "star_attn_abi_version")
+           "star_attn_phase2_partial_paged", "star_attn_decode_step_paged", "star_kv_write_rope",
+           "star_attn_phase1_rope", "star_attn_strerror", "star_attn_abi_version")
 
 
 class StarAttnError(RuntimeError):
@@ -50,6 +50,15 @@ class StarAttnDesc(ctypes.Structure):
                 ("anchor_len", ctypes.c_int64), ("tail_cap", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
 
+
+class StarRope(ctypes.Structure):
+    """Mirror of ``star_rope`` (device table pointers, rows, anchor mode)."""
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int64),
+                ("anchor_mode", ctypes.c_int32)]
+
+
+STAR_ROPE_ORIGINAL = 0
+STAR_ROPE_ADJACENT = 1
 
 _lib = None
 
@@ -76,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "star_attn_lse_merge": (ctypes.c_int, [D, I64, I32, P, P, P, I32, P, P]),
         "star_attn_decode_step": (ctypes.c_int, [D, P, P, I64, P, P, P, I64, P, P, P, I32, P, P]),
         "star_kv_page_bytes": (ctypes.c_size_t, [D]),
+        "star_kv_write_rope": (ctypes.c_int, [D, P, P, I64, P, P, I64, ctypes.POINTER(StarRope), P]),
+        "star_attn_phase1_rope": (ctypes.c_int, [D, P, P, P, ctypes.POINTER(StarRope), P, P]),
         "star_kv_write_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, P, I64, P]),
         "star_attn_phase2_partial_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, I64, P, P, P]),
         "star_attn_decode_step_paged": (ctypes.c_int, [D, P, P, P, I32, I64, P, P, P, I64, P, P, P,
@@ -341,3 +352,46 @@ def star_attn_decode_step_paged(desc, k_pages, v_pages, block_table, kv_len: int
         _ptr(lse_part, shp_p[:4], f32, "lse_part"), _ptr(o, shp_q, od, "o"), o_dtype,
         _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
     _check(st, "star_attn_decode_step_paged")
+
+
+# ---------------------------------------------------------------- rotary embedding
+
+def make_rope(cos, sin, anchor_mode: int = STAR_ROPE_ORIGINAL) -> StarRope:
+    """A ``star_rope`` over device fp32 tables ``[n_pos][head_dim/2]`` (torch
+    tensors, which the caller keeps alive)."""
+    torch = _torch()
+    for name, t in (("cos", cos), ("sin", sin)):
+        if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"rope {name}: a contiguous device float32 [n_pos, head_dim/2] tensor")
+    if cos.shape != sin.shape:
+        raise ValueError("rope: cos and sin differ in shape")
+    return StarRope(cos.data_ptr(), sin.data_ptr(), int(cos.shape[0]), anchor_mode)
+
+
+def _rope_arg(desc, rope):
+    if rope is None:
+        return None
+    if not isinstance(rope, StarRope):
+        raise TypeError("rope: a StarRope (make_rope)")
+    return ctypes.byref(rope)
+
+
+def star_kv_write_rope(desc, k_cache, v_cache, pos0: int, k_src, v_src, n_tok: int, rope,
+                       stream=None):
+    shp = (desc.batch, n_tok, desc.n_kv_heads, desc.head_dim)
+    elt = None if isinstance(k_src, int) else _elt(desc)
+    st = load_library().star_kv_write_rope(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        pos0, _ptr(k_src, shp, elt, "k_src"), _ptr(v_src, shp, elt, "v_src"), n_tok,
+        _rope_arg(desc, rope), _stream(stream))
+    _check(st, "star_kv_write_rope")
+
+
+def star_attn_phase1_rope(desc, k_cache, v_cache, q_ctx, rope, o_ctx, stream=None):
+    shp = (desc.batch, desc.ctx_len, desc.n_q_heads, desc.head_dim)
+    elt = None if isinstance(q_ctx, int) else _elt(desc)
+    st = load_library().star_attn_phase1_rope(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        _ptr(q_ctx, shp, elt, "q_ctx"), _rope_arg(desc, rope), _ptr(o_ctx, shp, elt, "o_ctx"),
+        _stream(stream))
+    _check(st, "star_attn_phase1_rope")

@@ -311,6 +311,42 @@ int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void*
   return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }
 
+// ---- rotary position embedding
+
+static int validate_rope(const Dims& d, const star_rope* rope) {
+  if (!rope || !rope->cos || !rope->sin) return STAR_ERR_INVALID_ARG;
+  if (rope->anchor_mode != STAR_ROPE_ORIGINAL && rope->anchor_mode != STAR_ROPE_ADJACENT)
+    return STAR_ERR_INVALID_ARG;
+  if (rope->n_pos < d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  return STAR_OK;
+}
+
+int star_kv_write_rope(const star_attn_desc* desc, void* k_cache, void* v_cache, int64_t pos0,
+                       const void* k_src, const void* v_src, int64_t n_tok,
+                       const star_rope* rope, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !k_src || !v_src || n_tok < 1) return STAR_ERR_INVALID_ARG;
+  st = validate_rope(d, rope);
+  if (st) return st;
+  if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  return launch_kv_write(d, k_cache, v_cache, pos0, k_src, v_src, n_tok, stream, nullptr, 0,
+                         rope->cos, rope->sin);
+}
+
+int star_attn_phase1_rope(const star_attn_desc* desc, const void* k_cache, const void* v_cache,
+                          const void* q_ctx, const star_rope* rope, void* o_ctx, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !q_ctx || !o_ctx) return STAR_ERR_INVALID_ARG;
+  st = validate_rope(d, rope);
+  if (st) return st;
+  return launch_phase1(d, k_cache, v_cache, q_ctx, o_ctx, stream, rope->cos, rope->sin,
+                       rope->anchor_mode);
+}
+
 const char* star_attn_strerror(int status) {
   switch (status) {
     case STAR_OK: return "success";

@@ -147,11 +147,15 @@ static inline void split_range(const Dims& d, const Plan& p, int64_t kv_len, int
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
 // table / maxp: a paged cache (kc, vc the page pools; table [B][maxp] page
 // ids), or null / 0 for the contiguous cache.
+// rope_cos / rope_sin: rotary tables [n_pos][D/2] (K rotated at its cache
+// row; phase 1's query at its position id, per rope_mode), or null.
 int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
                     const void* vs, int64_t n_tok, void* stream, const int32_t* table = nullptr,
-                    int32_t maxp = 0);
+                    int32_t maxp = 0, const float* rope_cos = nullptr,
+                    const float* rope_sin = nullptr);
 int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
-                  void* stream);
+                  void* stream, const float* rope_cos = nullptr, const float* rope_sin = nullptr,
+                  int rope_mode = 0);
 int launch_phase2_partial(const Dims& d, const Plan& p, const void* kc, const void* vc,
                           int64_t kv_len, const void* q, int64_t n_query, float* o_part,
                           float* lse_part, void* stream, const int32_t* table = nullptr,

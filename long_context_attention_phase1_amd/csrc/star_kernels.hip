@@ -161,6 +161,63 @@ __device__ __forceinline__ int64_t tile_elem_u(const PageMap& pm, int64_t rows, 
   }
 }
 
+// ---- rotary position embedding ---------------------------------------------
+//
+// Half-split pairing: element e < D/2 of a head vector turns together with
+// element e + D/2 by the angle whose cosine and sine are entry e of the
+// table row of the position (fp32 tables [n_pos][D/2]):
+//   y_e = x_e c - x_{e+D/2} s,   y_{e+D/2} = x_{e+D/2} c + x_e s.
+// fp32 arithmetic with every product and sum rounded on its own (no fused
+// multiply-add), then, for bf16 data, one round to nearest even.
+enum { kRopeNone = 0, kRopeOriginal = 1, kRopeAdjacent = 2 };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float rope_a(float x, float y, float c, float s) {
+#pragma clang fp contract(off)
+  return x * c - y * s;
+}
+__device__ __forceinline__ float rope_b(float x, float y, float c, float s) {
+#pragma clang fp contract(off)
+  return y * c + x * s;
+}
+
+// Two 16-byte chunks of bf16 (8 elements each): lo holds elements e .. e+7,
+// hi the elements e + D/2 ..; cr / sr point at table entries e .. e+7.
+__device__ __forceinline__ void rope_bf16x8(u32x4& lo, u32x4& hi, const float* cr,
+                                            const float* sr) {
+  const float4 c0 = *(const float4*)cr, c1 = *(const float4*)(cr + 4);
+  const float4 s0 = *(const float4*)sr, s1 = *(const float4*)(sr + 4);
+  const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  u32x4 nl, nh;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x0 = bf16_lo(lo[w]), x1 = bf16_hi(lo[w]);
+    const float y0 = bf16_lo(hi[w]), y1 = bf16_hi(hi[w]);
+    nl[w] = pack_bf16(rope_a(x0, y0, c[2 * w], sn[2 * w]), rope_a(x1, y1, c[2 * w + 1], sn[2 * w + 1]));
+    nh[w] = pack_bf16(rope_b(x0, y0, c[2 * w], sn[2 * w]), rope_b(x1, y1, c[2 * w + 1], sn[2 * w + 1]));
+  }
+  lo = nl;
+  hi = nh;
+}
+
+// The same for four fp32 elements per chunk (no rounding to bf16).
+__device__ __forceinline__ void rope_f32x4(u32x4& lo, u32x4& hi, const float* cr, const float* sr) {
+  const float4 c = *(const float4*)cr, sn = *(const float4*)sr;
+  const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+  u32x4 nl, nh;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = __uint_as_float(lo[w]), y = __uint_as_float(hi[w]);
+    nl[w] = __float_as_uint(rope_a(x, y, cc[w], ss[w]));
+    nh[w] = __float_as_uint(rope_b(x, y, cc[w], ss[w]));
+  }
+  lo = nl;
+  hi = nh;
+}
+
 // ---------------------------------------------------------------------------
 // kv_write
 // ---------------------------------------------------------------------------
@@ -169,12 +226,14 @@ struct KvArgs {
   void* vc;
   const void* ks;
   const void* vs;
+  const float* rope_cos;  // ROPE: K rows rotated at their cache row
+  const float* rope_sin;
   PageMap pm;
   int64_t pos0, n_tok, rows, t0;
   int32_t Hkv, nt;
 };
 
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
   constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;              // chunks per row
@@ -192,13 +251,40 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvArgs a) {
   T* vc = (T*)a.vc;
   const T* ks = (const T*)a.ks;
   const T* vs = (const T*)a.vs;
-  for (int u = tid; u < 64 * CPR; u += 256) {
-    const int rr = u / CPR, c = u % CPR;
-    const int64_t r = r0 + rr;
-    if (r >= r_lo && r < r_hi) {
-      const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
-      *(u32x4*)(kc + tb + rr * D + c * VEC) = *(const u32x4*)(ks + src);
-      *(u32x4*)(&vsm[rr][c * VEC]) = *(const u32x4*)(vs + src);
+  if constexpr (ROPE) {
+    // K: chunk c < CPR/2 and its partner chunk c + CPR/2, rotated at row r
+    constexpr int HC = CPR / 2;
+    for (int u = tid; u < 64 * HC; u += 256) {
+      const int rr = u / HC, c = u % HC;
+      const int64_t r = r0 + rr;
+      if (r >= r_lo && r < r_hi) {
+        const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
+        u32x4 lo = *(const u32x4*)(ks + src), hi = *(const u32x4*)(ks + src + D / 2);
+        const float* cr = a.rope_cos + r * (D / 2) + c * VEC;
+        const float* sr = a.rope_sin + r * (D / 2) + c * VEC;
+        if constexpr (sizeof(T) == 2) rope_bf16x8(lo, hi, cr, sr);
+        else rope_f32x4(lo, hi, cr, sr);
+        *(u32x4*)(kc + tb + rr * D + c * VEC) = lo;
+        *(u32x4*)(kc + tb + rr * D + c * VEC + D / 2) = hi;
+      }
+    }
+    for (int u = tid; u < 64 * CPR; u += 256) {
+      const int rr = u / CPR, c = u % CPR;
+      const int64_t r = r0 + rr;
+      if (r >= r_lo && r < r_hi) {
+        const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
+        *(u32x4*)(&vsm[rr][c * VEC]) = *(const u32x4*)(vs + src);
+      }
+    }
+  } else {
+    for (int u = tid; u < 64 * CPR; u += 256) {
+      const int rr = u / CPR, c = u % CPR;
+      const int64_t r = r0 + rr;
+      if (r >= r_lo && r < r_hi) {
+        const int64_t src = (((int64_t)s * a.n_tok + (r - a.pos0)) * a.Hkv + g) * D + c * VEC;
+        *(u32x4*)(kc + tb + rr * D + c * VEC) = *(const u32x4*)(ks + src);
+        *(u32x4*)(&vsm[rr][c * VEC]) = *(const u32x4*)(vs + src);
+      }
     }
   }
   __syncthreads();
@@ -241,6 +327,8 @@ struct WideArgs {
   int32_t BM;                           // rows per workgroup = 64 * (4 / HW)
   float scale, c2;                      // softmax scale and scale*log2(e)
   PageMap pm;                           // phase 2 on a paged cache
+  const float* rope_cos;                // ROPE (phase 1): tables [n_pos][D/2]
+  const float* rope_sin;
 };
 
 // Online-softmax update of one query-column tile from raw scores s[kt]
@@ -590,9 +678,10 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
 
 // Wave -> columns: wave w owns QT column tiles of 32 (query row, head) pairs.
 // The workgroup covers 256 columns: HW heads of one kv head x 64*(4/HW) rows.
-template <int D, int NW, int QT, bool PHASE1, bool PAGED>
+template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE>
 __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
+  static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
   constexpr int WPR = 2 / QT;  // waves per 64-row sub-tile of one head
@@ -654,17 +743,37 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   };
   const float c2 = a.c2;
 
-  // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g
+  // ---- query operand (B of S^T = K Q^T): column 32*qt + l32, d-chunk 2*ks + g.
+  // With a rotary embedding the query is turned at its position id, the
+  // context row less `shift`; chunk ks and chunk ks + KS/2 of a lane hold
+  // the element pairs (e, e + D/2) that turn together.
   u32x4 qop[QT][KS];
+  auto load_q = [&](int64_t shift) {
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int64_t r = wrow0 + 32 * qt + l32;
-    const bool ok = r < row_end;
-    const uint16_t* qp = a.q + (((int64_t)s * a.q_tokens + (ok ? r : 0)) * a.Hq + head) * D;
+    for (int qt = 0; qt < QT; ++qt) {
+      const int64_t r = wrow0 + 32 * qt + l32;
+      const bool ok = r < row_end;
+      const uint16_t* qp = a.q + (((int64_t)s * a.q_tokens + (ok ? r : 0)) * a.Hq + head) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[qt][ks] = ok ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
-  }
+      for (int ks = 0; ks < KS; ++ks)
+        qop[qt][ks] = ok ? ld16(qp + (2 * ks + g) * 8) : u32x4{0, 0, 0, 0};
+      if constexpr (ROPE != kRopeNone) {
+        const int64_t pos = ok ? r - shift : 0;
+        const float* cr = a.rope_cos + pos * (D / 2);
+        const float* sr = a.rope_sin + pos * (D / 2);
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks)
+          rope_bf16x8(qop[qt][ks], qop[qt][ks + KS / 2], cr + 8 * (2 * ks + g),
+                      sr + 8 * (2 * ks + g));
+      }
+    }
+  };
+  // adjacent anchor ids (i*b - a + j for anchor row j of block i): rotations
+  // compose, so the anchor pass keeps the cached keys and turns the query
+  // back by i*b - a instead
+  const int64_t q_shift =
+      (ROPE == kRopeAdjacent && PHASE1 && hiA > 0) ? (row0 / a.blk) * a.blk - a.anc : 0;
+  load_q(q_shift);
 
   f32x16 oacc[QT][DT];
 #pragma unroll
@@ -696,12 +805,14 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     if (i1 < i0) i1 = i0;
   }
   const int n_int = nAi + (int)(i1 - i0);
-  // interior tile j -> byte offset of its rows (clamped to the last tile)
+  // interior tiles j0 .. j0 + cnt - 1 (anchor tiles first, then the block's);
+  // tile j of the run -> byte offset of its rows (clamped to the last tile)
+  auto run_interior = [&](const int j0, const int cnt) {
   auto tile_off = [&](int j) -> int64_t {
-    j = j < n_int ? j : n_int - 1;
+    j = j0 + (j < cnt ? j : cnt - 1);
     return tile_at(j < nAi ? (int64_t)j : i0 + (j - nAi)) * 2;
   };
-
+  const int n_int = cnt;
   if (n_int > 0) {
     LaneOffsets<D, NW> lo;
     lo.init(l32, g, w, lane);
@@ -733,13 +844,16 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
   }
+  };
 
-  // ---- edge tiles: masked, synchronous, staged through registers with zero fill
+  // ---- edge tiles e0 .. e1 - 1 (the anchor's partial tile first, if any):
+  // masked, synchronous, staged through registers with zero fill
   const int n_edge = (a_edge ? 1 : 0) + (int)(i0 - bf) + (int)(bl - i1);
-  if (n_edge > 0) {
+  auto run_edges = [&](const int e0, const int e1) {
+  if (e1 > e0) {
     LaneOffsets<D, NW> lo;
     lo.init(l32, g, w, lane);
-    for (int e = 0; e < n_edge; ++e) {
+    for (int e = e0; e < e1; ++e) {
       int64_t kbase, klo, khi;
       bool causal;
       int k = e;
@@ -778,6 +892,20 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
       }
       block_sync_lds();
     }
+  }
+  };
+
+  if constexpr (ROPE == kRopeAdjacent) {
+    // the anchor (interior tiles, then its partial tile) with the turned-back
+    // query, then the block with the query at its own position
+    run_interior(0, nAi);
+    run_edges(0, a_edge ? 1 : 0);
+    if (q_shift != 0) load_q(0);
+    run_interior(nAi, n_int - nAi);
+    run_edges(a_edge ? 1 : 0, n_edge);
+  } else {
+    run_interior(0, n_int);
+    run_edges(0, n_edge);
   }
 
   // ---- epilogue: accumulator element i of tile dt is dimension 32*dt + 8*(i/4) + 4*g + i%4
@@ -1491,11 +1619,14 @@ struct F32Args {
   int32_t Hq, Hkv, G;
   float scale;
   PageMap pm;  // phase 2 on a paged cache
+  const float* rope_cos;  // ROPE (phase 1): tables [n_pos][D/2]
+  const float* rope_sin;
 };
 
-template <int D, bool PHASE1, bool PAGED>
+template <int D, bool PHASE1, bool PAGED, int ROPE>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
+  static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   constexpr int E = D / 64;  // output dimensions per lane
   __shared__ float qsm[4][D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1536,15 +1667,34 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
     else return t * 64 * D;
   };
   const float* qp = a.q + ((s * a.q_tokens + r) * a.Hq + h) * D;
-  for (int e = lane; e < D; e += 64) qsm[w][e] = qp[e];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  // the query in LDS; with a rotary embedding, turned at position id pos
+  auto load_q = [&](int64_t qpos) {
+    if constexpr (ROPE != kRopeNone) {
+      for (int e = lane; e < D / 2; e += 64) {
+        const float x = qp[e], y = qp[e + D / 2];
+        const float c = a.rope_cos[qpos * (D / 2) + e], sn = a.rope_sin[qpos * (D / 2) + e];
+        qsm[w][e] = rope_a(x, y, c, sn);
+        qsm[w][e + D / 2] = rope_b(x, y, c, sn);
+      }
+    } else {
+      for (int e = lane; e < D; e += 64) qsm[w][e] = qp[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  };
+  // adjacent anchor ids: the anchor pass turns the query back by i*b - a
+  const int64_t q_shift = (ROPE == kRopeAdjacent && PHASE1 && hiA > 0) ? (r / a.blk) * a.blk - a.anc : 0;
+  load_q(pos - q_shift);
 
   float m = kMinit, l = 0.0f, o[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) o[j] = 0.0f;
   for (int pass = 0; pass < 2; ++pass) {
     const int64_t lo = pass == 0 ? loA : loB, hi = pass == 0 ? hiA : hiB;
+    if (ROPE == kRopeAdjacent && pass == 1 && q_shift != 0) {
+      __builtin_amdgcn_wave_barrier();  // every lane's reads of the anchor pass are done
+      load_q(pos);
+    }
     for (int64_t base = lo; base < hi; base += 64) {
       const int64_t key = base + lane;
       const bool ok = key < hi;
@@ -1693,11 +1843,14 @@ constexpr int kWideWaves = 8;
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <bool PAGED>
+template <bool PAGED, bool ROPE>
 static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
-                         const void* vs, int64_t n_tok, const PageMap& pm, void* stream) {
+                         const void* vs, int64_t n_tok, const PageMap& pm, const float* rope_cos,
+                         const float* rope_sin, void* stream) {
   KvArgs a;
   a.pm = pm;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   a.kc = kc;
   a.vc = vc;
   a.ks = ks;
@@ -1712,24 +1865,29 @@ static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const 
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == STAR_BF16) {
     if (d.D == 128)
-      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 128, PAGED>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 128, PAGED, ROPE>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 64, PAGED>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_write_kernel<uint16_t, 64, PAGED, ROPE>), grid, dim3(256), 0, st, a);
   } else {
     if (d.D == 128)
-      hipLaunchKernelGGL((kv_write_kernel<float, 128, PAGED>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_write_kernel<float, 128, PAGED, ROPE>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((kv_write_kernel<float, 64, PAGED>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((kv_write_kernel<float, 64, PAGED, ROPE>), grid, dim3(256), 0, st, a);
   }
   return check_launch();
 }
 
 int launch_kv_write(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
                     const void* vs, int64_t n_tok, void* stream, const int32_t* table,
-                    int32_t maxp) {
+                    int32_t maxp, const float* rope_cos, const float* rope_sin) {
   const PageMap pm{table, maxp};
-  return table ? kv_write_impl<true>(d, kc, vc, pos0, ks, vs, n_tok, pm, stream)
-               : kv_write_impl<false>(d, kc, vc, pos0, ks, vs, n_tok, pm, stream);
+  if (rope_cos)  // rotary embedding: the contiguous cache
+    return kv_write_impl<false, true>(d, kc, vc, pos0, ks, vs, n_tok, pm, rope_cos, rope_sin,
+                                      stream);
+  return table ? kv_write_impl<true, false>(d, kc, vc, pos0, ks, vs, n_tok, pm, nullptr, nullptr,
+                                            stream)
+               : kv_write_impl<false, false>(d, kc, vc, pos0, ks, vs, n_tok, pm, nullptr, nullptr,
+                                             stream);
 }
 
 static F32Args f32_args(const Dims& d, const void* kc, const void* vc, const void* q) {
@@ -1749,17 +1907,20 @@ static F32Args f32_args(const Dims& d, const void* kc, const void* vc, const voi
   return a;
 }
 
-int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
-                  void* stream) {
+template <int ROPE>
+static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
+                       const float* rope_cos, const float* rope_sin, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == STAR_F32) {
     F32Args a = f32_args(d, kc, vc, q);
     a.o = (float*)o;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
     a.q_tokens = d.L;
     a.n_cols = (int64_t)d.B * d.L * d.Hq;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, true, false>), grid, dim3(256), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false, ROPE>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, true, false, ROPE>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -1783,15 +1944,25 @@ int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, 
   a.NRT = (int32_t)((d.blk + a.BM - 1) / a.BM);
   a.scale = d.scale;
   a.c2 = d.scale_log2;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
   const dim3 grid((unsigned)nwg);
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false, ROPE>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true, false>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true, false, ROPE>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
+}
+
+int launch_phase1(const Dims& d, const void* kc, const void* vc, const void* q, void* o,
+                  void* stream, const float* rope_cos, const float* rope_sin, int rope_mode) {
+  if (!rope_cos) return phase1_impl<kRopeNone>(d, kc, vc, q, o, nullptr, nullptr, stream);
+  if (rope_mode == STAR_ROPE_ADJACENT)
+    return phase1_impl<kRopeAdjacent>(d, kc, vc, q, o, rope_cos, rope_sin, stream);
+  return phase1_impl<kRopeOriginal>(d, kc, vc, q, o, rope_cos, rope_sin, stream);
 }
 
 static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, const void* vc,
@@ -1850,8 +2021,8 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.n_split = p.n_split;
     a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false, PAGED>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, false, PAGED>), grid, dim3(256), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<64, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
     return check_launch();
   }
   if (p.narrow && p.balanced) {
@@ -1921,10 +2092,10 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   a.pm = pm;
   const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }

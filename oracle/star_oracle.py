@@ -431,17 +431,22 @@ def _round_bf16(x32: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
-def rope_rotate_bf16(x: np.ndarray, cos_rows: np.ndarray, sin_rows: np.ndarray) -> np.ndarray:
-    """The rotation as a bf16 model stores its rotated keys: every product and
-    the sum or difference rounded to float32 (no fused multiply-add), then the
-    result rounded to bfloat16. Returns float64 values."""
+def rope_rotate_f32(x: np.ndarray, cos_rows: np.ndarray, sin_rows: np.ndarray) -> np.ndarray:
+    """The rotation in float32 arithmetic, every product and the sum or
+    difference rounded to float32 on its own (no fused multiply-add): the
+    rotated keys of an fp32 model. Returns float32."""
     x = np.asarray(x, dtype=np.float32)
     h = x.shape[-1] // 2
     c = np.asarray(cos_rows, dtype=np.float32)
     s = np.asarray(sin_rows, dtype=np.float32)
     lo, hi = x[..., :h], x[..., h:]
-    y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)
-    return _round_bf16(y).astype(np.float64)
+    return np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)
+
+
+def rope_rotate_bf16(x: np.ndarray, cos_rows: np.ndarray, sin_rows: np.ndarray) -> np.ndarray:
+    """The rotation as a bf16 model stores its rotated keys: the float32 form
+    above, then rounded to bfloat16. Returns float64 values."""
+    return _round_bf16(rope_rotate_f32(x, cos_rows, sin_rows)).astype(np.float64)
 
 
 def phase1_rope_positions(block_len: int, anchor_len: int, i: int, mode: int) -> np.ndarray:
@@ -485,4 +490,28 @@ def phase1_rope(q_ctx: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, block_l
                 S = np.where(visible, (Q @ K.T) * scale, -np.inf)
                 E = np.exp(S - S.max(axis=1, keepdims=True))
                 out[s, lo:hi, h] = (E @ V) / np.sum(E, axis=1, keepdims=True)
+    return out
+
+
+def phase1_rope_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
+                              rows: Sequence[int], block_len: int, anchor_len: int,
+                              scale: float, cos_tab: np.ndarray, sin_tab: np.ndarray,
+                              mode: int) -> np.ndarray:
+    """``phase1_rope`` for sampled context rows of the query heads of one kv
+    head (arguments as ``phase1_rows_one_head``, inputs not yet rotated):
+    each key is rotated at its position id (anchor rows per ``mode``), each
+    query at its row. Returns ``[n, h, d]``."""
+    out = np.zeros(q_rows.shape, dtype=np.float64)
+    for k, r in enumerate(rows):
+        r = int(r)
+        i = r // block_len
+        keys = phase1_key_rows(r, block_len, anchor_len)
+        n_anc = anchor_len if i > 0 else 0
+        pos = keys.copy()
+        if n_anc:
+            pos[:n_anc] = phase1_rope_positions(block_len, anchor_len, i, mode)
+        Kk = rope_rotate(np.asarray(K[keys], dtype=np.float64), cos_tab[pos], sin_tab[pos])
+        Qr = rope_rotate(np.asarray(q_rows[k], dtype=np.float64), cos_tab[r], sin_tab[r])
+        S = scale * (Qr @ Kk.T)
+        out[k], _ = _softmax_rows(S, np.asarray(V[keys], dtype=np.float64))
     return out

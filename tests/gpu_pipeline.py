@@ -83,6 +83,26 @@ class Pipeline:
             self._ws[key] = (n_split, o_part, lse_part, o, lse)
         return self._ws[key]
 
+    # -- rotary embedding (phase 1) ------------------------------------------
+    def rope(self, mode, theta=500000.0):
+        """Device rotary tables for every cache row and a star_rope over them."""
+        w = self.w
+        c, s_ = syn.rope_tables(w.head_dim, w.ctx_len + w.tail_cap, theta)
+        self.rope_host = (c, s_)
+        self._rope_dev = (torch.from_numpy(c).to(self.o_ctx.device),
+                          torch.from_numpy(s_).to(self.o_ctx.device))
+        return sa.make_rope(self._rope_dev[0], self._rope_dev[1], mode)
+
+    def write_context_rope(self, rope):
+        w = self.w
+        sa.star_kv_write_rope(self.desc, self.k_cache, self.v_cache, 0, self.dev["k_ctx"],
+                              self.dev["v_ctx"], w.ctx_len, rope)
+
+    def phase1_rope(self, rope):
+        sa.star_attn_phase1_rope(self.desc, self.k_cache, self.v_cache, self.dev["q_ctx"], rope,
+                                 self.o_ctx)
+        return self.o_ctx
+
     # the phase-2 calls on the cache (the paged pipeline overrides these three)
     def kv_write2(self, pos0, k, v, n_tok):
         sa.star_kv_write(self.desc, self.k_cache, self.v_cache, pos0, k, v, n_tok)

@@ -383,7 +383,10 @@ def pin_rope_bf16_is_torch_fp32_then_bf16(orc):
     c = torch.from_numpy(np.cos(ang).astype(np.float32))
     sn = torch.from_numpy(np.sin(ang).astype(np.float32))
     lo, hi = x[:, :16], x[:, 16:]
-    y = torch.cat([lo * c - hi * sn, hi * c + lo * sn], dim=1).to(torch.bfloat16).double()
+    y32 = torch.cat([lo * c - hi * sn, hi * c + lo * sn], dim=1)
+    _close(orc.rope_rotate_f32(x.numpy(), c.numpy(), sn.numpy()), y32.double().numpy(), 0.0,
+           "rope f32")
+    y = y32.to(torch.bfloat16).double()
     _close(orc.rope_rotate_bf16(x.numpy(), c.numpy(), sn.numpy()), y.numpy(), 0.0, "rope bf16")
     # cancellation: rounding each product to float32 gives 2^-23, the exact
     # difference 2^-23 (1 + 2^-7); both are bf16 values
@@ -477,6 +480,24 @@ def pin_phase1_rope_adjacent_is_query_shift(orc):
                 w = np.exp(sco - sco.max())
                 vv = np.concatenate([v[s, :a, g], v[s, i * b:r + 1, g]])
                 _close(got[s, r, h], (w @ vv) / w.sum(), 1e-12, f"shift row {r}")
+
+
+def pin_phase1_rope_sampled_rows_match_full(orc):
+    """The sampled-row form equals the full one (itself pinned above) on every
+    row, both modes."""
+    q, k, v, b, a, ang = _rope_case(47, L=21, b=8, a=5, Hq=4, Hkv=2)
+    L = q.shape[1]
+    sc = _scale(orc, q.shape[3])
+    ext = _angles(2 * L, q.shape[3]) * 1.3
+    rows = list(range(L))
+    for mode in (orc.ROPE_ORIGINAL, orc.ROPE_ADJACENT):
+        full = orc.phase1_rope(q, k, v, b, a, sc, np.cos(ext), np.sin(ext), mode)
+        for s in range(q.shape[0]):
+            for g in range(k.shape[2]):
+                hs = slice(2 * g, 2 * g + 2)
+                got = orc.phase1_rope_rows_one_head(q[s, :, hs], k[s, :, g], v[s, :, g], rows, b,
+                                                    a, sc, np.cos(ext), np.sin(ext), mode)
+                _close(got, full[s, :, hs], 1e-12, f"sampled rope rows, mode {mode}")
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -256,3 +256,55 @@ def test_paged_entry_points_validate_before_launching():
     bad = ctypes.byref(_desc(n_kv_heads=3))
     assert lib.star_kv_page_bytes(bad) == 0
     assert lib.star_kv_write_paged(bad, fake, fake, fake, need, 0, fake, fake, 1, None) == S
+
+
+def test_rope_struct_layout_matches_c_compiler():
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "star_attn.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %d %d\n", sizeof(star_rope), offsetof(star_rope, cos),
+         offsetof(star_rope, sin), offsetof(star_rope, n_pos), offsetof(star_rope, anchor_mode),
+         STAR_ROPE_ORIGINAL, STAR_ROPE_ADJACENT);
+  return 0;
+}'''
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "p.c")
+        exe = os.path.join(td, "p")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c,
+                        "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                              check=True).stdout.split()]
+    R = B.StarRope
+    want = ([ctypes.sizeof(R)] + [getattr(R, f).offset for f, _ in R._fields_]
+            + [B.STAR_ROPE_ORIGINAL, B.STAR_ROPE_ADJACENT])
+    assert got == want
+
+
+def test_rope_entry_points_validate_before_launching():
+    """Rotary entry points: a missing table or struct, an unknown anchor mode
+    or tables shorter than the cache's capacity fail before any launch; the
+    plain calls' checks still apply."""
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(_desc())  # capacity 131072 + 320 rows
+    E, S = B.STAR_ERR_INVALID_ARG, B.STAR_ERR_SHAPE
+    ok = B.StarRope(0x2000, 0x3000, 131072 + 320, B.STAR_ROPE_ADJACENT)
+    R = ctypes.byref
+    assert lib.star_attn_phase1_rope(d, fake, fake, fake, None, fake, None) == E
+    assert lib.star_attn_phase1_rope(d, fake, fake, fake, R(B.StarRope(0, 0x3000, 10 ** 6, 0)),
+                                     fake, None) == E
+    assert lib.star_attn_phase1_rope(d, fake, fake, fake, R(B.StarRope(0x2000, 0x3000, 10 ** 6, 2)),
+                                     fake, None) == E
+    assert lib.star_attn_phase1_rope(d, fake, fake, fake,
+                                     R(B.StarRope(0x2000, 0x3000, 131072 + 319, 0)), fake, None) == S
+    assert lib.star_attn_phase1_rope(d, fake, fake, None, R(ok), fake, None) == E
+    assert lib.star_kv_write_rope(d, fake, fake, 0, fake, fake, 1, None, None) == E
+    assert lib.star_kv_write_rope(d, fake, fake, 0, fake, fake, 1,
+                                  R(B.StarRope(0x2000, None, 10 ** 6, 0)), None) == E
+    assert lib.star_kv_write_rope(d, fake, fake, 131072 + 320, fake, fake, 1, R(ok), None) == S
+    assert lib.star_kv_write_rope(d, fake, fake, 0, fake, fake, 0, R(ok), None) == E
+    bad = ctypes.byref(_desc(anchor_len=20000))  # anchor longer than the block
+    assert lib.star_attn_phase1_rope(bad, fake, fake, fake, R(ok), fake, None) == S

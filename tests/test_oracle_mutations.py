@@ -118,8 +118,8 @@ MUTANTS = [
      "u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16",
      "u = (u + 0x8000) >> 16 << 16"),
     ("rope_bf16_fused_in_float64",
-     "y = np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)",
-     "y = np.concatenate([(lo.astype(np.float64) * c) - (hi.astype(np.float64) * s), (hi.astype(np.float64) * c) + (lo.astype(np.float64) * s)], axis=-1).astype(np.float32)"),
+     "return np.concatenate([(lo * c) - (hi * s), (hi * c) + (lo * s)], axis=-1).astype(np.float32)",
+     "return np.concatenate([(lo.astype(np.float64) * c) - (hi.astype(np.float64) * s), (hi.astype(np.float64) * c) + (lo.astype(np.float64) * s)], axis=-1).astype(np.float32)"),
     ("rope_adjacent_no_anchor_shift",
      "return j if mode == ROPE_ORIGINAL else i * block_len - anchor_len + j",
      "return j if mode == ROPE_ORIGINAL else i * block_len + j"),
@@ -141,6 +141,12 @@ MUTANTS = [
     ("rope_phase1_normalised_by_total",
      "out[s, lo:hi, h] = (E @ V) / np.sum(E, axis=1, keepdims=True)",
      "out[s, lo:hi, h] = (E @ V) / np.sum(E)"),
+    ("rope_rows_anchor_at_original_ids",
+     "            pos[:n_anc] = phase1_rope_positions(block_len, anchor_len, i, mode)",
+     "            pos[:n_anc] = phase1_rope_positions(block_len, anchor_len, i, ROPE_ORIGINAL)"),
+    ("rope_rows_query_at_block_start",
+     "Qr = rope_rotate(np.asarray(q_rows[k], dtype=np.float64), cos_tab[r], sin_tab[r])",
+     "Qr = rope_rotate(np.asarray(q_rows[k], dtype=np.float64), cos_tab[i * block_len], sin_tab[i * block_len])"),
     ("rope_phase1_anchor_on_block0",
      "            if i > 0:\n                anc_rows = np.arange(anchor_len, dtype=np.int64)",
      "            if i >= 0:\n                anc_rows = np.arange(anchor_len, dtype=np.int64)"),
