@@ -91,9 +91,6 @@ STAR_HD static inline int64_t inner_boundaries_below(int64_t L, int64_t blk, int
   if (L < x && L % wg_rows != 0) ++c;
   return c;
 }
-int validate_desc(const star_attn_desc* d, Dims* out);
-int validate_phase2(const Dims& d, int64_t kv_len, int64_t n_query);
-Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query);
 
 // Split sigma of a plan -> rows [lo, hi) (lo == hi: empty) and host id
 // (context block index, or n_blocks for the tail).

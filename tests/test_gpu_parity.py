@@ -2,7 +2,7 @@
 
 Small workloads checked element by element: several tiles, ragged last
 blocks, block starts not aligned to the 64-row cache tile, anchors shorter
-than the block, GQA 1:1 / 2:1 / 4:1 / 8:1, head_dim 64 and 128, bf16 and
+than the block, one-row blocks and a one-token context, GQA 1:1 / 2:1 / 4:1 / 8:1, head_dim 64 and 128, bf16 and
 fp32, the peaked-softmax input, a context shorter than one block, both
 phase-2 kernels (<= 32 and > 32 query columns), empty splits and every
 decode step. Tolerances: max-abs 1e-5 (fp32 workloads) and 2e-2 (bf16
@@ -47,6 +47,13 @@ CASES = {
     # per-wave decode kernel at d = 64, two sequences, GQA 8:1, a 24-column
     # query step; block starts 448 and 1344 fall inside 128-row ranges
     "balanced_b2_g8_d64": W("bal_b2", 2, 16, 2, 64, 1536, 448, 200, 3, 2, "bf16", seed=16),
+    # degenerate partitions: one-row blocks and a one-row anchor (every row
+    # sees token 0 and itself), a one-token context, one-row blocks with a
+    # query step of more than 32 columns, and the fp32 path
+    "b1_a1": W("b1_a1", 1, 4, 2, 128, 70, 1, 1, 3, 2, "bf16", seed=17),
+    "ctx1": W("ctx1", 1, 2, 1, 64, 1, 1, 1, 2, 2, "bf16", seed=18),
+    "b1_wide_tail": W("b1_wide", 1, 4, 2, 128, 50, 1, 1, 40, 2, "bf16", seed=20),
+    "f32_b1": W("f32_b1", 1, 2, 2, 64, 40, 1, 1, 2, 1, "f32", seed=19),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
@@ -111,7 +118,8 @@ def test_phase2_query_and_decode_match_oracle(runs, name):
 
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g1_unaligned_a_lt_b", "g2_d64_wide_tail",
                                   "g8_narrow", "f32_gqa_d128", "long_tail_wide",
-                                  "ragged_empty_split", "balanced_bnd", "balanced_b2_g8_d64"])
+                                  "ragged_empty_split", "balanced_bnd", "balanced_b2_g8_d64",
+                                  "b1_a1", "ctx1", "b1_wide_tail", "f32_b1"])
 def test_partials_are_the_hosts_replies(runs, name):
     """Each split's (vector, scalar) equals the oracle's host reply on that range."""
     p, _, _, _ = _pipeline(runs, name)
@@ -246,7 +254,8 @@ def test_binding_rejects_wrong_buffers():
 
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g8_narrow", "peaked", "ragged_empty_split",
                                   "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks",
-                                  "balanced_bnd", "balanced_b2_g8_d64"])
+                                  "balanced_bnd", "balanced_b2_g8_d64", "b1_a1", "ctx1",
+                                  "f32_b1"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
     decode loop and against the three separate calls, every step."""
