@@ -6,7 +6,7 @@
     and, given the JSON line that the profiled bench.py printed, the figures
     of that same run measured with HIP events.
 
-``python -m long_context_attention_phase1_amd.profiling traffic FETCH_DIR WRITE_DIR OUT``
+``python -m long_context_attention_phase1_amd.profiling traffic FETCH_DIR WRITE_DIR OUT.json OUT.txt -- CMD``
     reads two ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of
     ``bench.py --copy-calibration`` and writes, per kernel and launch shape,
     the HBM bytes per launch. Both counters are in KiB per dispatch; each is
