@@ -100,7 +100,7 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
 def load_traffic(*kernels):
     """HBM bytes per launch, summed over the given kernels, from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
-    kernel source; else None."""
+    native library source (csrc/); else None."""
     try:
         doc = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):

@@ -101,7 +101,10 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
   p.n_groups = p.narrow ? d.B * d.Hkv : d.B * d.Hkv * d.HQ;
   p.n_qtiles = p.narrow ? 1 : (int32_t)cdiv(n_query, (int64_t)kColsPerWave * d.RW);
   if (p.narrow && balanced_plan(d, kv_len, &p)) return p;
-  // decode: ~one long-running workgroup per CU; many query rows: 8 per CU
+  // about one long-running workgroup per CU. Many query rows: every split
+  // writes Tq x Hq x d fp32 partials that the merge reads back, so shorter
+  // splits cost more partial traffic than they gain in balance (the 128K
+  // query step: 0.33 ms at 257 splits per kv head, 0.21 ms at 33)
   const int64_t total = p.narrow ? kNarrowWorkgroups : kTargetWorkgroups;
   const int64_t min_len = p.narrow ? 512 : 256;
   int64_t target = total / ((int64_t)p.n_groups * p.n_qtiles);

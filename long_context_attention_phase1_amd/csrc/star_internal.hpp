@@ -12,7 +12,8 @@ constexpr int kTile = STAR_KV_TILE;   // rows of a KV-cache tile
 constexpr int kWaves = 4;             // waves per workgroup of the MFMA kernels
 constexpr int kColsPerWave = 64;      // query columns (row, head pairs) per wave
 constexpr int kNarrowCols = 32;       // columns of the single-tile decode kernel
-constexpr int kTargetWorkgroups = 2048;  // phase-2 planner target, many query rows (8 per CU)
+constexpr int kTargetWorkgroups = 256;   // phase-2 planner target, many query rows (one per CU:
+                                         // fewer, longer splits write fewer fp32 partials)
 constexpr int kNarrowWorkgroups = 256;   // phase-2 planner target, decode (one per CU)
 constexpr int kDecodeWaves = 4 * 256;    // balanced plan: ranges per launch (4 waves per CU)
 constexpr int kSlice = 32;               // balanced plan: ranges are whole 32-key slices

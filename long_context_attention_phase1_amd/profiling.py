@@ -35,11 +35,18 @@ from collections import defaultdict
 
 COPY_BYTES = 1 << 30
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(PKG, "csrc", "star_kernels.hip")
+CSRC = os.path.join(PKG, "csrc")
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over every file of the native library (kernels, launchers,
+    planner): a change to any of them can change what a launch does."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        path = os.path.join(CSRC, name)
+        if os.path.isfile(path) and name.endswith((".hip", ".cpp", ".hpp", ".h")):
+            h.update(name.encode() + b"\0" + open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def short_name(name: str) -> str:
@@ -72,7 +79,7 @@ def _bench_lines(path: str):
 def stats(d: str, out: str, command: str, bench_json: str = None) -> None:
     rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}",
-             f"# kernel source sha256[:16]: {source_sha()}",
+             f"# native source (csrc/) sha256[:16]: {source_sha()}",
              f"{'kernel':58s} {'calls':>6s} {'total ms':>10s} {'avg us':>10s} "
              f"{'min us':>10s} {'max us':>10s} {'%':>6s}"]
     for r in rows:
@@ -127,7 +134,7 @@ def traffic(fetch_dir: str, write_dir: str, out_json: str, out_txt: str, command
              f"# calibration: device-to-device copy of {COPY_BYTES} B (runtime blit kernel) -> "
              f"bytes = FETCH_SIZE KiB x 1024 x {f_scale:.4f} + WRITE_SIZE KiB x 1024 x "
              f"{w_scale:.4f}",
-             f"# kernel source sha256[:16]: {sha}",
+             f"# native source (csrc/) sha256[:16]: {sha}",
              f"{'kernel':40s} {'grid':>9s} {'disp':>5s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} "
              f"{'bytes/launch':>13s}"]
     best = {}
@@ -172,7 +179,7 @@ def counters(out_txt: str, dirs, command: str, kernels=None) -> None:
     lines = ["# rocprofv3 --pmc counters per kernel (summed over the XCDs and shader engines;",
              "# GRBM_GUI_ACTIVE averaged over the runs that took it)",
              f"# command: {command}",
-             f"# kernel source sha256[:16]: {source_sha()}"]
+             f"# native source (csrc/) sha256[:16]: {source_sha()}"]
     for k, cl in vals.items():
         c = {name: sum(v) / len(v) for name, v in cl.items()}
         gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS  # active cycles of one XCD
