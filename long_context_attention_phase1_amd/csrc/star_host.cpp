@@ -71,7 +71,7 @@ static int64_t gcd64(int64_t a, int64_t b) {
 // per wave (four waves per workgroup, one workgroup per CU), at most one host
 // boundary inside each. Returns false when the shape does not allow it.
 static bool balanced_plan(const Dims& d, int64_t kv_len, Plan* p) {
-  if (d.dtype != STAR_BF16 || d.blk % kTile != 0 || d.L % kTile != 0) return false;
+  if (d.dtype != STAR_BF16) return false;
   const int64_t groups = (int64_t)d.B * d.Hkv;
   int64_t w = kDecodeWaves / groups;
   if (w < 1) w = 1;

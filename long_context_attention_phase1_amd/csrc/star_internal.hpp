@@ -38,13 +38,13 @@ struct Dims {
 // blk_len rows and the tail into tail_splits of tail_len rows; one workgroup
 // per split.
 //
-// Balanced plan (decode kernel, bf16, tile-aligned blocks and context): the
-// rows [0, kv_len) of every (sequence, kv head) are cut into n_wg equal
-// ranges of wg_rows rows (whole 32-key slices), one wave each, four waves per
-// workgroup, so that the whole grid is resident at once. A range holds at
-// most one host boundary (a block start, or the context/tail edge); a range
-// that holds one yields two splits, one on each side. Splits are numbered in
-// row order.
+// Balanced plan (decode kernel, bf16): the rows [0, kv_len) of every
+// (sequence, kv head) are cut into n_wg equal ranges of wg_rows rows (whole
+// 32-key slices), one wave each, four waves per workgroup, so that the whole
+// grid is resident at once. A range holds at most one host boundary (a block
+// start, or the context/tail edge), anywhere in it, on a slice edge or not;
+// a range that holds one yields two splits, one on each side. Splits are
+// numbered in row order.
 struct Plan {
   int32_t narrow;         // 1: single-column-tile decode kernel, 0: wide kernel
   int32_t per_block;      // splits per context block

@@ -7,7 +7,8 @@
 //                       output) and by phase-2 partials with many query rows
 //   attn_decode_kernel  split-KV decode partials (<= 32 query columns), balanced
 //                       plan: one cache range per wave, no barriers
-//   attn_narrow_kernel  the same for the blockwise plan (unaligned shapes)
+//   attn_narrow_kernel  the same for the blockwise plan (blocks shorter than a
+//                       balanced range)
 //   attn_f32_kernel     fp32 path (VALU) for both phases
 //   lse_merge_kernel    exact softmax renormalisation of the partials (one
 //                       workgroup per output row)
@@ -1342,7 +1343,9 @@ __device__ __forceinline__ uint32_t vs_off(int e, int kc) {
   return (uint32_t)(e * 64 + ((kc ^ ((e >> 2) & 3)) << 4));
 }
 
-template <int D, bool FUSED, bool PAGED>
+// MID: a host boundary may fall inside a 32-key slice (a context or block
+// length off the slice grid); only then is the slice-splitting path compiled.
+template <int D, bool FUSED, bool PAGED, bool MID>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   using Dg = DecodeGeo<D>;
   constexpr int KS = Dg::KS, DT = Dg::DT;
@@ -1432,7 +1435,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   const int n_sl = (int)((hi - lo + 31) / 32);
   int64_t vis = pos0 + 1 < hi ? pos0 + 1 : hi;
   const int n_in = vis > lo ? (int)((vis - lo) / 32) : 0;
-  const int sb = bnd >= 0 ? (int)((bnd - lo) / 32) : 0x7fffffff;  // first slice of split 2
+  // split 2 starts in slice sb; if bnd is not on a slice edge, that slice's
+  // keys below bnd still belong to split 1
+  const int sb = bnd >= 0 ? (int)((bnd - lo) / 32) : 0x7fffffff;
+  const bool bnd_mid = MID && bnd >= 0 && (bnd - lo) % 32 != 0;
   const char* Kc = (const char*)K;
   const char* Vc = (const char*)V;
   // slice i (clamped to the last one): K rows from row lo + 32 i; V^T from the
@@ -1509,23 +1515,26 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   };
   int32_t npg = 0;
   if constexpr (PAGED) npg = slice_page(2);
+  // close split 1 (its state moves to oprev) and open split 2
+  auto switch_split = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      oprev[0][dt] = oacc[0][dt];
+      oacc[0][dt] = f32x16{};
+    }
+    mprev = m[0];
+    lprev = l[0];
+    m[0] = kMinit;
+    l[0] = 0.0f;
+    switched = true;
+  };
   auto step = [&](int i, int st) {
     // slice i has landed; slice i + 1 (if any) stays in flight
     if (i + 1 < n_sl) wait_vmcnt<Dg::PER>();
     else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
-    if (i >= sb && !switched) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        oprev[0][dt] = oacc[0][dt];
-        oacc[0][dt] = f32x16{};
-      }
-      mprev = m[0];
-      lprev = l[0];
-      m[0] = kMinit;
-      l[0] = 0.0f;
-      switched = true;
-    }
+    const bool split_here = bnd_mid && i == sb;
+    if (i >= sb && !switched && !split_here) switch_split();
     char* sm = ring + st * Dg::SB;
     const bool masked = i >= n_in;
     const int64_t key0 = lo + 32 * (int64_t)i;
@@ -1548,16 +1557,32 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
         if (key >= hi || key > cpos || !cvalid) sc[0][ii] = -INFINITY;
       }
     }
-    float mx[1];
-    slice_max3<1>(sc, mx);
-    rescale_top<1, DT>(mx, m, l, oacc, c2);
-    u32x4 p[1][2];
-    slice_exp2<1>(sc, m, l, p, c2);
+    // online-softmax update of the current split with scores t
+    auto update = [&](f32x16 (&t)[1]) {
+      float mx[1];
+      slice_max3<1>(t, mx);
+      rescale_top<1, DT>(mx, m, l, oacc, c2);
+      u32x4 p[1][2];
+      slice_exp2<1>(t, m, l, p, c2);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        oacc[0][dt] = mfma_bf16(lds16(sm + vq[kb] + dt * 32 * 64), p[0][kb], oacc[0][dt]);
+        for (int kb = 0; kb < 2; ++kb)
+          oacc[0][dt] = mfma_bf16(lds16(sm + vq[kb] + dt * 32 * 64), p[0][kb], oacc[0][dt]);
+    };
+    if (split_here) {
+      // the host boundary falls inside this slice: its keys below bnd end
+      // split 1, the rest start split 2 (both are written rows)
+      f32x16 s1[1] = {sc[0]};
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        if (key0 + acc_key(ii, g) >= bnd) s1[0][ii] = -INFINITY;
+        else sc[0][ii] = -INFINITY;
+      }
+      update(s1);
+      switch_split();
+    }
+    update(sc);
     // this wave's reads of the stage are complete before it is refilled
     if (i + 2 < n_sl) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -1579,17 +1604,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   }
   wait_vmcnt<0>();
   // a split that starts at bnd after the last slice is empty
-  if (bnd >= 0 && !switched) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      oprev[0][dt] = oacc[0][dt];
-      oacc[0][dt] = f32x16{};
-    }
-    mprev = m[0];
-    lprev = l[0];
-    m[0] = kMinit;
-    l[0] = 0.0f;
-  }
+  if (bnd >= 0 && !switched) switch_split();
 
   // ---- partials straight from registers: column l32's 16 values per dt
   // tile are rows 32 dt + 8 (i / 4) + 4 g + (i % 4)
@@ -2009,13 +2024,20 @@ static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, cons
   return a;
 }
 
-template <bool FUSED, bool PAGED>
-static void launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+template <bool FUSED, bool PAGED, bool MID>
+static void launch_decode_mid(const Dims& d, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.NG * a.WPG));
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<128, FUSED, PAGED>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_decode_kernel<128, FUSED, PAGED, MID>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<64, FUSED, PAGED>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_decode_kernel<64, FUSED, PAGED, MID>), grid, dim3(256), 0, st, a);
+}
+
+template <bool FUSED, bool PAGED>
+static void launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+  // host boundaries (block starts, the context end) off the 32-key slice grid
+  if (d.L % kSlice != 0 || d.blk % kSlice != 0) launch_decode_mid<FUSED, PAGED, true>(d, a, st);
+  else launch_decode_mid<FUSED, PAGED, false>(d, a, st);
 }
 
 template <bool PAGED>

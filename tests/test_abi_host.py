@@ -220,6 +220,25 @@ def test_decode_plan_is_balanced_at_128k(kv_len):
     assert sum(lens) == kv_len
 
 
+@pytest.mark.parametrize("kv_len", [125003 + 65, 125003 + 320])
+def test_decode_plan_is_balanced_on_a_ragged_context(kv_len):
+    """A context that is not a multiple of the 32-key slice (125,003 rows, the
+    ragged sweep) still gets the balanced plan: the tail start falls inside a
+    slice of one range, which yields two splits."""
+    d = _desc(n_q_heads=32, n_kv_heads=8, ctx_len=125003, block_len=16384, anchor_len=16384,
+              tail_cap=320)
+    n = sa.star_attn_phase2_plan(d, kv_len, 1)
+    r = -(-(-(-kv_len // 128)) // 32) * 32
+    rng = [sa.star_attn_phase2_split_range(d, kv_len, 1, s) for s in range(n)]
+    assert max(hi - lo for lo, hi, _ in rng) <= r
+    assert n <= 128 + 8
+    # the split that ends the context and the one that starts the tail meet at
+    # an unaligned row inside one range
+    ends = [hi for lo, hi, _ in rng]
+    assert 125003 in ends and 125003 % 32 != 0
+    assert sum(hi - lo for lo, hi, _ in rng) == kv_len
+
+
 def test_paged_entry_points_validate_before_launching():
     """Paged calls: page size, and every argument check (null pools or table,
     a table too short for the cache's capacity, the contiguous calls' shape

@@ -39,8 +39,11 @@ CASES = {
     "g4_d64_many_blocks": W("g4_d64", 1, 8, 2, 64, 1024, 128, 128, 40, 1, "bf16", seed=8),
     # tail longer than one split: early query rows see nothing of the second tail split
     "long_tail_wide": W("long_tail", 1, 4, 2, 128, 128, 64, 64, 300, 1, "bf16", seed=13),
-    # last block shorter than the split length: its second split is empty
-    "ragged_empty_split": W("ragged_empty", 1, 4, 1, 128, 2100, 1024, 300, 2, 2, "bf16", seed=14),
+    # balanced decode plan on a ragged context: the tail start (2172) falls
+    # inside a 32-key slice of the range [2048, 2176), and the last range
+    # [2176, 2180) holds query rows only, so the first four queries see none
+    # of it (an empty split: lse = -inf, o = 0)
+    "ragged_empty_split": W("ragged_empty", 1, 4, 1, 128, 2172, 1024, 300, 8, 2, "bf16", seed=14),
     # balanced decode plan: 512-row ranges with a block start (1088) and the
     # tail start (2176) strictly inside, a 16-column query step, tail < 1 tile
     "balanced_bnd": W("balanced_bnd", 1, 8, 2, 128, 2176, 1088, 512, 4, 3, "bf16", seed=15),
