@@ -244,7 +244,11 @@ def main():
     pg = "true" if args.paged else "false"
     rp = {"none": 0, "original": 1, "adjacent": 2}[args.rope]
     kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}>"
-    kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}>", f"lse_merge_kernel<{w.head_dim}>")
+    # the decode kernel's instantiation that splits a 32-key slice at a host
+    # boundary serves contexts and blocks off the slice grid
+    mid = "true" if (w.ctx_len % 32 or w.block_len % 32) else "false"
+    kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}, {mid}>",
+              f"lse_merge_kernel<{w.head_dim}>")
     t1, t2 = load_traffic(kname1), load_traffic(*kname2)
     out = {
         "metric": METRIC,
