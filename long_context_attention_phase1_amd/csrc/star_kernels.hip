@@ -575,10 +575,13 @@ template <int D, int NW, int QT, int ST, int KT>
 __device__ __forceinline__ void pv_slice(const char* smem, const LaneOffsets<D, NW>& lo,
                                          const u32x4 (&p)[QT][2], f32x16 (&o)[QT][Geo<D, NW>::DT]) {
   using Gm = Geo<D, NW>;
+  // the first half of P (keys 0-15) feeds the first DT MFMAs, so the exps
+  // of the second half have that long to land; every O tile still adds
+  // half 0 then half 1
 #pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int dt = 0; dt < Gm::DT; ++dt) {
       const u32x4 vop = lds16(smem + lo.vq[KT][kb] + (ST * Gm::VBYTES + dt * 32 * 128));
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mfma_bf16(vop, p[qt][kb], o[qt][dt]);
