@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama8b_128k_peaked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the peak probes (libstarpeaks.so) run after the timed steps")
     ap.add_argument("--threads", type=int, default=None)
     ap.add_argument("--rope", choices=["none", "original", "adjacent"], default="none",
                     help="phase 1 with the rotary embedding fused (K rotated by the context "
@@ -250,6 +252,13 @@ def main():
     kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}, {mid}>",
               f"lse_merge_kernel<{w.head_dim}>")
     t1, t2 = load_traffic(kname1), load_traffic(*kname2)
+    # measured peaks (after the timed region): the rates each roofline is also
+    # read against, beside the published peaks
+    measured = None
+    if not args.no_peaks:
+        from long_context_attention_phase1_amd import peaks
+        measured = peaks.measure(device=p.k_cache.device)
+        torch.cuda.synchronize()
     out = {
         "metric": METRIC,
         "value": ctx_tok_s,
@@ -286,6 +295,11 @@ def main():
                                            "new K/V row written, one fp32 reply per host "
                                            "written and re-read, output row written"},
     }
+    if measured is not None:
+        out["measured_peaks"] = measured
+        if w.dtype == "bf16":
+            out["roofline"]["frac_of_measured"] = p1_tflops / measured["mfma_bf16"]["value"]
+        out["roofline_phase2"]["frac_of_measured"] = dec_gbs / measured["hbm_read"]["value"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)
     print(json.dumps(out), flush=True)

@@ -38,14 +38,16 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
 
+# the attention library's sources: a change to any of them (kernels,
+# launchers, planner) can change what a launch does
+LIB_SOURCES = ("star_host.cpp", "star_internal.hpp", "star_kernels.hip")
+
+
 def source_sha() -> str:
-    """sha256[:16] over every file of the native library (kernels, launchers,
-    planner): a change to any of them can change what a launch does."""
+    """sha256[:16] over the attention library's sources."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        path = os.path.join(CSRC, name)
-        if os.path.isfile(path) and name.endswith((".hip", ".cpp", ".hpp", ".h")):
-            h.update(name.encode() + b"\0" + open(path, "rb").read())
+    for name in sorted(LIB_SOURCES):
+        h.update(name.encode() + b"\0" + open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
 
