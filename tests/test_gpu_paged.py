@@ -20,7 +20,7 @@ from tests.gpu_pipeline import PagedPipeline, Pipeline, to_host_f64
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
-TOL_LSE = {"bf16": 2e-3, "f32": 1e-5}
+TOL_LSE = {"bf16": 4e-3, "f32": 1e-5}  # as in test_gpu_parity.py
 
 W = syn.Workload
 CASES = {

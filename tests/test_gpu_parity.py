@@ -23,7 +23,11 @@ from tests.gpu_pipeline import Pipeline, to_host_f64
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "f32": 1e-5}
-TOL_LSE = {"bf16": 2e-3, "f32": 1e-5}
+# the kernels sum the bf16-rounded P (the same weights that P.V uses): each
+# term is off by at most 2^-8 relative (8 significant bits, round to
+# nearest), so the sum is too, and the lse by at most -ln(1 - 2^-8) = 3.92e-3,
+# a bound that a row dominated by one key can approach
+TOL_LSE = {"bf16": 4e-3, "f32": 1e-5}
 
 W = syn.Workload
 CASES = {
