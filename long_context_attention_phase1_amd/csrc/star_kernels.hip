@@ -332,43 +332,6 @@ struct WideArgs {
   const float* rope_sin;
 };
 
-// Online-softmax update of one query-column tile from raw scores s[kt]
-// (NKT 32-key slices); returns the packed bf16 P operands.
-template <int NKT, int DT>
-__device__ __forceinline__ void softmax_update(f32x16 (&s)[NKT], float& m, float& l,
-                                               f32x16 (&o)[DT], u32x4 (&p)[NKT][2], float c2) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(m, mx);
-  const float alpha = fast_exp2((m - m_new) * c2);
-  const float mc = m_new * c2;
-  float rs = 0.0f;
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = fast_exp2(fmaf(s[kt][i], c2, -mc));
-      s[kt][i] = e;
-      rs += e;
-    }
-  l = l * alpha + rs;
-  m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int b = kb * 8;
-      p[kt][kb] = u32x4{pack_bf16(s[kt][b + 0], s[kt][b + 1]), pack_bf16(s[kt][b + 2], s[kt][b + 3]),
-                        pack_bf16(s[kt][b + 4], s[kt][b + 5]), pack_bf16(s[kt][b + 6], s[kt][b + 7])};
-    }
-}
-
 // max / sum with the lane 32 apart (v_permlane32_swap).
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
