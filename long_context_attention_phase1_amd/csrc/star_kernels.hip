@@ -1839,6 +1839,13 @@ constexpr int kWideWaves = 8;
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// HIP takes a grid as a 32-bit count of work-items: a launch whose
+// workgroups would not fit is refused (STAR_ERR_SHAPE) before anything is
+// enqueued, rather than truncated.
+static bool grid_fits(int64_t wgs, int threads) {
+  return wgs >= 1 && wgs <= (int64_t)0xFFFFFFFF / threads;
+}
+
 template <bool PAGED, bool ROPE>
 static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
                          const void* vs, int64_t n_tok, const PageMap& pm, const float* rope_cos,
@@ -1857,6 +1864,7 @@ static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const 
   a.t0 = pos0 / 64;
   a.nt = (int32_t)((pos0 + n_tok - 1) / 64 - a.t0 + 1);
   a.Hkv = d.Hkv;
+  if (!grid_fits((int64_t)a.nt * d.B * d.Hkv, 256)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)((int64_t)a.nt * d.B * d.Hkv));
   hipStream_t st = (hipStream_t)stream;
   if (d.dtype == STAR_BF16) {
@@ -1914,6 +1922,7 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.rope_sin = rope_sin;
     a.q_tokens = d.L;
     a.n_cols = (int64_t)d.B * d.L * d.Hq;
+    if (!grid_fits((a.n_cols + 3) / 4, 256)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
     if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false, ROPE>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_f32_kernel<64, true, false, ROPE>), grid, dim3(256), 0, st, a);
@@ -1943,6 +1952,7 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
   const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
+  if (!grid_fits(nwg, 64 * kWideWaves)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)nwg);
   if (d.D == 128)
     hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false, ROPE>), grid,
@@ -1991,19 +2001,21 @@ static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, cons
 }
 
 template <bool FUSED, bool PAGED, bool MID>
-static void launch_decode_mid(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+static int launch_decode_mid(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+  if (!grid_fits((int64_t)a.NG * a.WPG, 256)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)((int64_t)a.NG * a.WPG));
   if (d.D == 128)
     hipLaunchKernelGGL((attn_decode_kernel<128, FUSED, PAGED, MID>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_decode_kernel<64, FUSED, PAGED, MID>), grid, dim3(256), 0, st, a);
+  return STAR_OK;
 }
 
 template <bool FUSED, bool PAGED>
-static void launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
+static int launch_decode(const Dims& d, const DecodeArgs& a, hipStream_t st) {
   // host boundaries (block starts, the context end) off the 32-key slice grid
-  if (d.L % kSlice != 0 || d.blk % kSlice != 0) launch_decode_mid<FUSED, PAGED, true>(d, a, st);
-  else launch_decode_mid<FUSED, PAGED, false>(d, a, st);
+  if (d.L % kSlice != 0 || d.blk % kSlice != 0) return launch_decode_mid<FUSED, PAGED, true>(d, a, st);
+  return launch_decode_mid<FUSED, PAGED, false>(d, a, st);
 }
 
 template <bool PAGED>
@@ -2023,6 +2035,7 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.per_block = p.per_block;
     a.n_split = p.n_split;
     a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
+    if (!grid_fits((a.n_cols + 3) / 4, 256)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)((a.n_cols + 3) / 4));
     if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_f32_kernel<64, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
@@ -2031,8 +2044,8 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   if (p.narrow && p.balanced) {
     DecodeArgs a = decode_args(d, p, kc, vc, kv_len, q, n_query, o_part, lse_part);
     a.pm = pm;
-    launch_decode<false, PAGED>(d, a, st);
-    return check_launch();
+    const int rc = launch_decode<false, PAGED>(d, a, st);
+    return rc ? rc : check_launch();
   }
   if (p.narrow) {
     NarrowArgs a{};
@@ -2058,6 +2071,7 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.scale = d.scale;
     a.c2 = d.scale_log2;
     a.pm = pm;
+    if (!grid_fits((int64_t)a.NG * p.n_split, 256)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
     if (d.D == 128)
       hipLaunchKernelGGL((attn_narrow_kernel<128, false, PAGED>), grid, dim3(256), 0, st, a);
@@ -2093,6 +2107,7 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   a.scale = d.scale;
   a.c2 = d.scale_log2;
   a.pm = pm;
+  if (!grid_fits((int64_t)a.NG * a.NRT * p.n_split, 64 * kWideWaves)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
   if (d.D == 128)
     hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone>), grid,
@@ -2123,7 +2138,8 @@ static int decode_step_impl(const Dims& d, const Plan& p, void* kc, void* vc, in
     a.k_new = (const uint16_t*)k_new;
     a.v_new = (const uint16_t*)v_new;
     a.pm = pm;
-    launch_decode<true, PAGED>(d, a, st);
+    const int rc = launch_decode<true, PAGED>(d, a, st);
+    if (rc) return rc;
   } else {
     NarrowArgs a{};
     a.k = (const uint16_t*)kc;
@@ -2150,6 +2166,7 @@ static int decode_step_impl(const Dims& d, const Plan& p, void* kc, void* vc, in
     a.k_new = (const uint16_t*)k_new;
     a.v_new = (const uint16_t*)v_new;
     a.pm = pm;
+    if (!grid_fits((int64_t)a.NG * p.n_split, 256)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)((int64_t)a.NG * p.n_split));
     if (d.D == 128)
       hipLaunchKernelGGL((attn_narrow_kernel<128, true, PAGED>), grid, dim3(256), 0, st, a);
@@ -2183,6 +2200,7 @@ int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const floa
   a.rows = (int64_t)d.B * n_query * d.Hq;
   a.n_split = n_split;
   a.o_f32 = o_dtype == STAR_F32;
+  if (!grid_fits(a.rows, 256)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)a.rows);
   hipStream_t st = (hipStream_t)stream;
   if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);

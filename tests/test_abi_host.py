@@ -327,3 +327,22 @@ def test_rope_entry_points_validate_before_launching():
     assert lib.star_kv_write_rope(d, fake, fake, 0, fake, fake, 0, R(ok), None) == E
     bad = ctypes.byref(_desc(anchor_len=20000))  # anchor longer than the block
     assert lib.star_attn_phase1_rope(bad, fake, fake, fake, R(ok), fake, None) == S
+
+
+def test_launches_too_large_for_one_grid_are_refused_before_launching():
+    """Shapes that pass validation but whose grid would not fit HIP's 32-bit
+    work-item count come back as STAR_ERR_SHAPE from the launcher's own check,
+    before any HIP call (no GPU here: a call that reached HIP would fail with
+    STAR_ERR_HIP instead)."""
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    S = B.STAR_ERR_SHAPE
+    # phase 1: 8 kv heads x 2^28 row tiles x 512 threads
+    big = _desc(ctx_len=1 << 34, block_len=1 << 20, anchor_len=1 << 20, tail_cap=64)
+    assert lib.star_attn_phase1(ctypes.byref(big), fake, fake, fake, fake, None) == S
+    # the context write of all 2^34 rows: 2^28 tiles x 8 kv heads x 256 threads
+    assert lib.star_kv_write(ctypes.byref(big), fake, fake, 0, fake, fake, 1 << 34, None) == S
+    # phase-2 partials on one-row blocks: one split per block
+    tiny = _desc(ctx_len=1 << 28, block_len=1, anchor_len=1, tail_cap=64)
+    assert lib.star_attn_phase2_partial(ctypes.byref(tiny), fake, fake, (1 << 28) + 64, fake, 64,
+                                        fake, fake, None) == S
