@@ -359,6 +359,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // accumulators are rescaled (by exp2((m_old - m_new) * c2)) only then; the
 // final O / l uses the same m, so the result is unchanged.
 constexpr float kTau = 8.0f;
+constexpr int kXcds = 8;  // MI355X: accelerator complex dies, one L2 each
 constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -668,10 +669,22 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  // ---- which (group, work item) this workgroup is
+  // ---- which (group, work item) this workgroup is. Workgroups go to the
+  // XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2.
+  // bid % NG keeps a group on one XCD; phase 1 with more groups than XCDs
+  // (several sequences, or query-head sub-groups) also runs each XCD's groups
+  // one after another, so its L2 holds one group's K/V at a time.
   const int64_t bid = blockIdx.x;
-  const int gidx = (int)(bid % a.NG);
-  const int64_t work = bid / a.NG;
+  int gidx;
+  int64_t work;
+  if (PHASE1 && a.NG > kXcds && a.NG % kXcds == 0) {
+    const int64_t per_group = (int64_t)a.n_blocks * a.NRT, i = bid / kXcds;
+    gidx = (int)(bid % kXcds) + kXcds * (int)(i / per_group);
+    work = i % per_group;
+  } else {
+    gidx = (int)(bid % a.NG);
+    work = bid / a.NG;
+  }
   const int hq = gidx % a.HQ, t2 = gidx / a.HQ;
   const int kvh = t2 % a.Hkv, s = t2 / a.Hkv;
   const int wsub = w % WPR, wh = w / WPR;  // 32*QT-row piece, (head, 64-row sub-tile)
@@ -681,12 +694,15 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   int64_t row0, row_end, hiA = 0, loB, hiB, pos_off;
   int32_t sigma = 0;
   if (PHASE1) {
-    // heaviest tiles first: anchored blocks by descending row tile, then block 0
+    // anchored blocks one after another, each by descending row tile (the
+    // heaviest first), then block 0: the workgroups that an XCD runs at once
+    // are neighbouring row tiles of one block, and share the anchor's and
+    // the block's K/V tiles in its L2
     const int64_t n1 = (int64_t)(a.n_blocks - 1) * a.NRT;
     int64_t i, rt;
     if (work < n1) {
-      rt = a.NRT - 1 - work / (a.n_blocks - 1);
-      i = 1 + work % (a.n_blocks - 1);
+      rt = a.NRT - 1 - work % a.NRT;
+      i = 1 + work / a.NRT;
     } else {
       rt = a.NRT - 1 - (work - n1);
       i = 0;
