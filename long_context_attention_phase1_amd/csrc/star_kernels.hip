@@ -671,14 +671,15 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
 
   // ---- which (group, work item) this workgroup is. Workgroups go to the
   // XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2.
-  // bid % NG keeps a group on one XCD; phase 1 with more groups than XCDs
-  // (several sequences, or query-head sub-groups) also runs each XCD's groups
-  // one after another, so its L2 holds one group's K/V at a time.
+  // bid % NG keeps a group on one XCD; with more groups than XCDs (several
+  // sequences, or query-head sub-groups) each XCD also runs its groups one
+  // after another, so its L2 holds one group's K/V at a time.
   const int64_t bid = blockIdx.x;
   int gidx;
   int64_t work;
-  if (PHASE1 && a.NG > kXcds && a.NG % kXcds == 0) {
-    const int64_t per_group = (int64_t)a.n_blocks * a.NRT, i = bid / kXcds;
+  if (a.NG > kXcds && a.NG % kXcds == 0) {
+    const int64_t per_group = PHASE1 ? (int64_t)a.n_blocks * a.NRT : (int64_t)a.NRT * a.n_split;
+    const int64_t i = bid / kXcds;
     gidx = (int)(bid % kXcds) + kXcds * (int)(i / per_group);
     work = i % per_group;
   } else {
