@@ -64,8 +64,9 @@ def decode_bytes(w, kv_len: int) -> float:
     return append + kv + q + parts + out
 
 
-def cpu_baseline(w, inputs, budget_s: float = 12.0):
-    """The oracle (as it stands) on a bounded sample of the same workload."""
+def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    phase-1 context rows (the headline unit), then decode tokens."""
     import numpy as np
 
     from long_context_attention_phase1_amd import synthetic as syn
@@ -91,19 +92,45 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0):
             break
     wall = time.perf_counter() - t0
     cpu = time.process_time() - c0
+
+    # decode tokens of sequence 0 in order: each attends to the context and
+    # the tail rows up to itself (the dense definition of a phase-2 row)
+    Kall = [np.concatenate([Ks[g], wide(inputs["k_tail"][0, :, g])]) for g in range(w.n_kv_heads)]
+    Vall = [np.concatenate([Vs[g], wide(inputs["v_tail"][0, :, g])]) for g in range(w.n_kv_heads)]
+    del Ks, Vs
+    t1, c1 = time.perf_counter(), time.process_time()
+    steps = 0
+    for t in range(w.n_decode):
+        row = w.n_query + t
+        for g in range(w.n_kv_heads):
+            q = wide(inputs["q_tail"][0, row:row + 1, g * G:(g + 1) * G])
+            orc.phase2_rows_one_head(q, Kall[g], Vall[g], [w.ctx_len + row], sc)
+        steps += 1
+        if time.perf_counter() - t1 > decode_budget_s:
+            break
+    dwall = time.perf_counter() - t1
+    dcpu = time.process_time() - c1
     return {"value": done / wall, "unit": "ctx tokens/s", "cores": max(1, round(cpu / wall)),
             "kind": "oracle",
             "sample": f"phase-1 fp64 oracle on {done} context rows drawn uniformly (seed 0) "
-                      f"from sequence 0, all {w.n_q_heads} query heads, {wall:.1f} s wall"}
+                      f"from sequence 0, all {w.n_q_heads} query heads, {wall:.1f} s wall",
+            "decode": {"value": dwall * 1e6 / steps, "unit": "µs/token",
+                       "cores": max(1, round(dcpu / dwall)),
+                       "sample": f"dense fp64 oracle rows of the first {steps} decode tokens "
+                                 f"of sequence 0, all {w.n_q_heads} query heads, "
+                                 f"{dwall:.1f} s wall"}}
 
 
-def load_traffic(*kernels):
+def load_traffic(config: dict, *kernels):
     """HBM bytes per launch, summed over the given kernels, from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
-    native library source (csrc/); else None."""
+    native library source (csrc/) and on this bench configuration (workload,
+    cache, rotary mode: the launch shapes depend on it); else None."""
     try:
         doc = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
+        return None
+    if doc.get("_bench_config") != config:
         return None
     from long_context_attention_phase1_amd.profiling import source_sha
     sha = source_sha()
@@ -134,8 +161,8 @@ def copy_calibration():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama8b_128k_peaked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
@@ -251,7 +278,8 @@ def main():
     mid = "true" if (w.ctx_len % 32 or w.block_len % 32) else "false"
     kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}, {mid}>",
               f"lse_merge_kernel<{w.head_dim}>")
-    t1, t2 = load_traffic(kname1), load_traffic(*kname2)
+    bcfg = {"workload": args.workload, "paged": bool(args.paged), "rope": args.rope}
+    t1, t2 = load_traffic(bcfg, kname1), load_traffic(bcfg, *kname2)
     # measured peaks (after the timed region): the rates each roofline is also
     # read against, beside the published peaks
     measured = None

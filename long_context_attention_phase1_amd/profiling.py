@@ -13,6 +13,9 @@
     scaled by what it reads on the plain device-to-device copy of known size
     that the calibration run performs first (``COPY_BYTES`` read and written
     once), so the figures are in the same units as the algorithmic bytes.
+    The bench configuration the runs measured (workload, cache, rotary mode:
+    ``bench_config`` of their command) is recorded beside the figures, which
+    hold for that configuration only.
 
 ``python -m long_context_attention_phase1_amd.profiling counters OUT.txt DIR... -- CMD``
     sums the SQ_* / GRBM_GUI_ACTIVE counters of the given ``rocprofv3 --pmc``
@@ -118,6 +121,21 @@ def _calibration(disp, counter: str) -> float:
     return COPY_BYTES / (sum(vals) / len(vals) * 1024)
 
 
+def bench_config(command: str) -> dict:
+    """The workload options of a bench.py command line (its defaults where
+    absent): the launch shapes, hence the traffic, depend on them."""
+    import shlex
+
+    args = shlex.split(command)
+    cfg = {"workload": "llama8b_128k_peaked", "paged": "--paged" in args, "rope": "none"}
+    for i, a in enumerate(args[:-1]):
+        if a == "--workload":
+            cfg["workload"] = args[i + 1]
+        elif a == "--rope":
+            cfg["rope"] = args[i + 1]
+    return cfg
+
+
 def traffic(fetch_dir: str, write_dir: str, out_json: str, out_txt: str, commands) -> None:
     fetch = _dispatches(fetch_dir, "FETCH_SIZE")
     write = _dispatches(write_dir, "WRITE_SIZE")
@@ -128,11 +146,16 @@ def traffic(fetch_dir: str, write_dir: str, out_json: str, out_txt: str, command
         if i in write and write[i][0] == k and "_kernel<" in k and not k.startswith("at::"):
             groups[(k, grid)].append((fv, write[i][2]))
     sha = source_sha()
+    cfgs = [bench_config(c.split(" -- ", 1)[-1]) for c in commands]
+    if any(c != cfgs[0] for c in cfgs):
+        raise ValueError("the FETCH_SIZE and WRITE_SIZE runs measured different bench configurations")
     doc = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_scale": f_scale,
                             "write_scale": w_scale, "copy_kernel": "__amd_rocclr_copyBuffer",
-                            "commands": list(commands)}}
+                            "commands": list(commands)},
+           "_bench_config": cfgs[0]}
     lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch)",
              *[f"# command: {c}" for c in commands],
+             f"# bench configuration: {json.dumps(cfgs[0])} (the figures hold for it only)",
              f"# calibration: device-to-device copy of {COPY_BYTES} B (runtime blit kernel) -> "
              f"bytes = FETCH_SIZE KiB x 1024 x {f_scale:.4f} + WRITE_SIZE KiB x 1024 x "
              f"{w_scale:.4f}",
