@@ -9,7 +9,8 @@ Prints ONE JSON line. ``value`` is the phase-1 context throughput (tokens/s)
 measured inside the timed steps; the decode figure (µs per step and per
 token) is reported beside it. ``roofline`` is for the dominant kernel
 (phase 1, MFMA-bound), from HIP events recorded on the launch stream around
-every phase-1 launch in the timed steps; ``roofline_phase2`` is for the
+every phase-1 launch in the timed steps; ``roofline_query`` is for the
+query step against the larger of its two bounds; ``roofline_phase2`` is for the
 decode step (HBM-bound), from events around the whole decode loop (every
 step's two launches: append + partials, merge) divided by the steps. ``cpu_baseline`` is the fp64 oracle timed on a bounded
 sample on the host.
@@ -62,6 +63,45 @@ def decode_bytes(w, kv_len: int) -> float:
     parts = 2.0 * w.batch * w.n_q_heads * hosts * (w.head_dim + 1) * 4
     out = w.batch * w.n_q_heads * (w.head_dim * elt + 4)
     return append + kv + q + parts + out
+
+
+def query_work(w):
+    """Algorithmic (FLOP, HBM bytes) of the query step: the n_query tokens'
+    K/V rows written, K+V rows [0, ctx_len + n_query) and the queries read
+    once, every host's reply (one fp32 vector and one scalar per query row
+    and head, for each context block and the tail) written and read back,
+    the outputs and their LSEs written. FLOP: 4*d per visible (query, key)
+    pair; query j sees rows [0, ctx_len + j]."""
+    elt = 2 if w.dtype == "bf16" else 4
+    T, L = w.n_query, w.ctx_len
+    pairs = T * L + T * (T + 1) // 2
+    flop = 4.0 * w.head_dim * pairs * w.batch * w.n_q_heads
+    append = 2.0 * w.batch * T * w.n_kv_heads * w.head_dim * elt
+    kv = 2.0 * w.batch * w.n_kv_heads * (L + T) * w.head_dim * elt
+    q = w.batch * T * w.n_q_heads * w.head_dim * elt
+    parts = 2.0 * w.batch * T * w.n_q_heads * (w.n_blocks + 1) * (w.head_dim + 1) * 4
+    out = w.batch * T * w.n_q_heads * (w.head_dim * elt + 4)
+    return flop, append + kv + q + parts + out
+
+
+def query_roofline(w, q_ms: float) -> dict:
+    """The query step against the larger of its two bounds (MFMA time of its
+    FLOP at the bf16 peak, HBM time of its bytes at 8 TB/s)."""
+    flop, nbytes = query_work(w)
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t = q_ms * 1e-3
+    if t_hbm >= t_mfma:
+        r = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": flop / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["frac_other_bound"] = min(t_mfma, t_hbm) / t
+    r["kernel"] = "query step: kv_write + partials + merge"
+    r["algorithmic"] = (f"{flop:.4e} FLOP (4*d per visible pair) and {nbytes:.4e} B "
+                        f"(K+V rows read once, n_query K/V rows written, replies, outputs)")
+    return r
 
 
 def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0):
@@ -272,7 +312,7 @@ def main():
 
     pg = "true" if args.paged else "false"
     rp = {"none": 0, "original": 1, "adjacent": 2}[args.rope]
-    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}>"
+    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}, false>"
     # the decode kernel's instantiation that splits a 32-key slice at a host
     # boundary serves contexts and blocks off the slice grid
     mid = "true" if (w.ctx_len % 32 or w.block_len % 32) else "false"
@@ -322,12 +362,18 @@ def main():
                             "algorithmic": "per decode step: K+V rows [0, kv_len) and q read, "
                                            "new K/V row written, one fp32 reply per host "
                                            "written and re-read, output row written"},
+        "roofline_query": query_roofline(w, q_ms),
     }
     if measured is not None:
         out["measured_peaks"] = measured
         if w.dtype == "bf16":
             out["roofline"]["frac_of_measured"] = p1_tflops / measured["mfma_bf16"]["value"]
         out["roofline_phase2"]["frac_of_measured"] = dec_gbs / measured["hbm_read"]["value"]
+        rq = out["roofline_query"]
+        if rq["bound"] == "hbm":
+            rq["frac_of_measured"] = rq["achieved"] / measured["hbm_read"]["value"]
+        elif w.dtype == "bf16":
+            rq["frac_of_measured"] = rq["achieved"] / measured["mfma_bf16"]["value"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs)
     print(json.dumps(out), flush=True)

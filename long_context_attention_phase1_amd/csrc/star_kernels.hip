@@ -656,9 +656,14 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
 
 // Wave -> columns: wave w owns QT column tiles of 32 (query row, head) pairs.
 // The workgroup covers 256 columns: HW heads of one kv head x 64*(4/HW) rows.
-template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE>
+// KVNT: the interior K/V tiles are read with the non-temporal policy. Phase 2
+// takes it when each split's keys are read by one workgroup; when several
+// workgroups read them (query-head sub-groups, query tiles), and in phase 1,
+// the default policy lets L2 serve the re-reads.
+template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE, bool KVNT>
 __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
+  static_assert(!(PHASE1 && KVNT), "phase 1 reuses its tiles through L2");
   static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
@@ -673,11 +678,19 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   // XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2.
   // bid % NG keeps a group on one XCD; with more groups than XCDs (several
   // sequences, or query-head sub-groups) each XCD also runs its groups one
-  // after another, so its L2 holds one group's K/V at a time.
+  // after another, so its L2 holds one group's K/V at a time. In phase 2,
+  // where the query-head sub-groups and query tiles of a kv head read the
+  // same split, an XCD takes every work item of a kv head, with the readers
+  // of one split next to each other (so they run at the same time).
   const int64_t bid = blockIdx.x;
   int gidx;
   int64_t work;
-  if (a.NG > kXcds && a.NG % kXcds == 0) {
+  if (!PHASE1 && a.HQ * a.NRT > 1 && (a.NG / a.HQ) % kXcds == 0) {
+    const int64_t per_kv = (int64_t)a.HQ * a.NRT * a.n_split;
+    const int64_t i = bid / kXcds, r = i % per_kv;
+    gidx = ((int)(bid % kXcds) + kXcds * (int)(i / per_kv)) * a.HQ + (int)(r % a.HQ);
+    work = r / a.HQ;
+  } else if (a.NG > kXcds && a.NG % kXcds == 0) {
     const int64_t per_group = PHASE1 ? (int64_t)a.n_blocks * a.NRT : (int64_t)a.NRT * a.n_split;
     const int64_t i = bid / kXcds;
     gidx = (int)(bid % kXcds) + kXcds * (int)(i / per_group);
@@ -812,9 +825,9 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     lo.init(l32, g, w, lane);
     const char* Kc = (const char*)K;
     const char* Vc = (const char*)V;
-    dma_stage_asm<D, NW, 0, !PHASE1>(smem, Kc + tile_off(0), Vc + tile_off(0), lo, w);
-    dma_stage_asm<D, NW, 1, !PHASE1>(smem, Kc + tile_off(1), Vc + tile_off(1), lo, w);
-    dma_stage_asm<D, NW, 2, !PHASE1>(smem, Kc + tile_off(2), Vc + tile_off(2), lo, w);
+    dma_stage_asm<D, NW, 0, KVNT>(smem, Kc + tile_off(0), Vc + tile_off(0), lo, w);
+    dma_stage_asm<D, NW, 1, KVNT>(smem, Kc + tile_off(1), Vc + tile_off(1), lo, w);
+    dma_stage_asm<D, NW, 2, KVNT>(smem, Kc + tile_off(2), Vc + tile_off(2), lo, w);
     wait_vmcnt<2 * Gm::PER>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS read moves above the wait
@@ -823,16 +836,16 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
     slice_max3<QT>(sc, mx);
     for (int t = 0; t < n_int; t += 4) {
-      interior_stage<D, NW, QT, 0, !PHASE1>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 0, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
                                             Kc + tile_off(t + 3), Vc + tile_off(t + 3), w);
       if (t + 1 >= n_int) break;
-      interior_stage<D, NW, QT, 1, !PHASE1>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 1, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
                                             Kc + tile_off(t + 4), Vc + tile_off(t + 4), w);
       if (t + 2 >= n_int) break;
-      interior_stage<D, NW, QT, 2, !PHASE1>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 2, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
                                             Kc + tile_off(t + 5), Vc + tile_off(t + 5), w);
       if (t + 3 >= n_int) break;
-      interior_stage<D, NW, QT, 3, !PHASE1>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 3, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
                                             Kc + tile_off(t + 6), Vc + tile_off(t + 6), w);
     }
     wait_vmcnt<0>();
@@ -1972,10 +1985,10 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
   if (!grid_fits(nwg, 64 * kWideWaves)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)nwg);
   if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false, ROPE>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false, ROPE, false>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true, false, ROPE>), grid,
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, true, false, ROPE, false>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
@@ -2126,12 +2139,20 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   a.pm = pm;
   if (!grid_fits((int64_t)a.NG * a.NRT * p.n_split, 64 * kWideWaves)) return STAR_ERR_SHAPE;
   const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
-  if (d.D == 128)
-    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone>), grid,
-                       dim3(64 * kWideWaves), 0, st, a);
+  // one reader per split: a non-temporal stream; several: L2 serves the rest
+  const bool kv_nt = a.HQ * a.NRT == 1;
+  if (d.D == 128 && kv_nt)
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone, true>),
+                       grid, dim3(64 * kWideWaves), 0, st, a);
+  else if (d.D == 128)
+    hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone, false>),
+                       grid, dim3(64 * kWideWaves), 0, st, a);
+  else if (kv_nt)
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone, true>),
+                       grid, dim3(64 * kWideWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone>), grid,
-                       dim3(64 * kWideWaves), 0, st, a);
+    hipLaunchKernelGGL((attn_wide_kernel<64, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone, false>),
+                       grid, dim3(64 * kWideWaves), 0, st, a);
   return check_launch();
 }
 

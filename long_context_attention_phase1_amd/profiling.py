@@ -236,7 +236,7 @@ def _main(argv):
     elif argv[:1] == ["counters"] and "--" in argv:
         i = argv.index("--")
         counters(argv[1], argv[2:i], " ".join(argv[i + 1:]),
-                 kernels={"attn_wide_kernel<128, 8, 1, true, false, 0>"})
+                 kernels={"attn_wide_kernel<128, 8, 1, true, false, 0, false>"})
     elif argv[:1] == ["traffic"] and "--" in argv:
         i = argv.index("--")
         cmds = " ".join(argv[i + 1:]).split(" ;; ")

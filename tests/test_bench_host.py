@@ -51,3 +51,21 @@ def test_traffic_is_only_attached_to_the_measured_configuration():
     other = dict(cfg, workload="llama8b_32k" if cfg["workload"] != "llama8b_32k" else "llama8b_1m")
     assert bench.load_traffic(other, kernel) is None
     assert bench.load_traffic(dict(cfg, paged=not cfg["paged"]), kernel) is None
+
+
+def test_query_step_work_and_bound():
+    # 32K and 128K sit below the ridge (HBM-bound), 1M well below, the
+    # four-sequence 64-head shape above it (MFMA-bound)
+    for name, bound in (("llama8b_32k", "hbm"), ("llama8b_128k_peaked", "hbm"),
+                        ("llama8b_1m", "hbm"), ("llama70b_256k_b4", "mfma")):
+        w = syn.workload(name)
+        flop, nbytes = bench.query_work(w)
+        T, L = w.n_query, w.ctx_len
+        assert flop == 4.0 * w.head_dim * w.batch * w.n_q_heads * sum(L + j + 1 for j in range(T))
+        cache = 2.0 * w.batch * w.n_kv_heads * (L + T) * w.head_dim * 2
+        assert cache < nbytes < cache * 1.2  # plus the replies of 64 rows x 9-33 hosts
+        r = bench.query_roofline(w, 1.0)
+        assert r["bound"] == bound
+        t_bound = max(flop / 2.5e15, nbytes / 8e12)
+        assert abs(r["frac"] - t_bound / 1e-3) < 1e-12
+        assert r["frac_other_bound"] <= r["frac"]
