@@ -36,6 +36,11 @@ CASES = {
     # fp32 path
     "tiny_f32": syn.WORKLOADS["tiny_f32"],
     "f32_gqa_d128": W("f32_gqa", 1, 4, 2, 128, 130, 64, 10, 3, 2, "f32", seed=7),
+    # eight kv groups (2 sequences x 4 kv heads), GQA 8:1 in two head
+    # sub-groups, a 320-column query step: both sub-groups read each split,
+    # so the wide kernel keeps a kv head's work items on one XCD and reads
+    # K/V with the default cache policy
+    "kv_major_g8": W("kv_major", 2, 32, 4, 128, 640, 256, 256, 40, 1, "bf16", seed=21),
 }
 
 

@@ -61,6 +61,11 @@ CASES = {
     "ctx1": W("ctx1", 1, 2, 1, 64, 1, 1, 1, 2, 2, "bf16", seed=18),
     "b1_wide_tail": W("b1_wide", 1, 4, 2, 128, 50, 1, 1, 40, 2, "bf16", seed=20),
     "f32_b1": W("f32_b1", 1, 2, 2, 64, 40, 1, 1, 2, 1, "f32", seed=19),
+    # eight kv groups (2 sequences x 4 kv heads), GQA 8:1 in two head
+    # sub-groups, a 320-column query step: both sub-groups read each split,
+    # so the wide kernel keeps a kv head's work items on one XCD and reads
+    # K/V with the default cache policy
+    "kv_major_g8": W("kv_major", 2, 32, 4, 128, 640, 256, 256, 40, 1, "bf16", seed=21),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
