@@ -63,6 +63,9 @@ STAR_ROPE_ADJACENT = 1
 _lib = None
 
 
+ABI_VERSION = 1  # STAR_ATTN_ABI_VERSION of include/star_attn.h that these signatures follow
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libstarattn.so (once). Raises if it has not been built."""
     global _lib
@@ -97,6 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
+    if lib.star_attn_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.star_attn_abi_version()}, this binding "
+                          f"marshals version {ABI_VERSION}: rebuild the library")
     _lib = lib
     return lib
 

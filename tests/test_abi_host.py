@@ -346,3 +346,10 @@ def test_launches_too_large_for_one_grid_are_refused_before_launching():
     tiny = _desc(ctx_len=1 << 28, block_len=1, anchor_len=1, tail_cap=64)
     assert lib.star_attn_phase2_partial(ctypes.byref(tiny), fake, fake, (1 << 28) + 64, fake, 64,
                                         fake, fake, None) == S
+
+
+def test_binding_follows_the_header_abi_version():
+    import re
+    from long_context_attention_phase1_amd import binding
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "star_attn.h")).read()
+    assert int(re.search(r"#define STAR_ATTN_ABI_VERSION (\d+)", hdr).group(1)) == binding.ABI_VERSION
