@@ -229,7 +229,7 @@ def main():
 
     import long_context_attention_phase1_amd as sa
     from long_context_attention_phase1_amd import synthetic as syn
-    from tests.gpu_pipeline import PagedPipeline, Pipeline
+    from long_context_attention_phase1_amd.pipeline import PagedPipeline, Pipeline
 
     w = syn.workload(args.workload)
     torch.cuda.set_device(0)

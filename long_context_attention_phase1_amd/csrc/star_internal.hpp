@@ -142,6 +142,183 @@ static inline void split_range(const Dims& d, const Plan& p, int64_t kv_len, int
   *host = d.n_blocks;
 }
 
+// ---- launch geometry and workgroup -> work maps
+//
+// Shared by the kernels (which call the STAR_HD maps on blockIdx) and by the
+// host replay in the tests, which walks every workgroup of a launch through
+// the same functions and checks that every work item is done once and every
+// address lies inside its buffer.
+
+constexpr int kXcds = 8;       // MI355X: accelerator complex dies, one L2 each;
+                               // workgroup i of a launch runs on XCD i % 8
+constexpr int kWideWaves = 8;  // waves per wide-kernel workgroup (two per SIMD)
+
+STAR_HD static inline int64_t cdiv_hd(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Wide-kernel launch: NG groups (sequence, kv head, head sub-group) times NRT
+// row tiles of BM rows (phase 1: of every block; phase 2: of the query rows)
+// times n_blocks blocks (phase 1) or n_split splits (phase 2).
+struct WideGeom {
+  int32_t phase1;
+  int32_t NG, NRT, BM, HQ;
+  int32_t n_blocks, n_split;
+  int64_t grid;  // workgroups
+};
+
+static inline WideGeom phase1_geom(const Dims& d) {
+  WideGeom g{};
+  g.phase1 = 1;
+  g.HQ = d.HQ;
+  g.BM = kColsPerWave * d.RW;
+  g.NG = d.B * d.Hkv * d.HQ;
+  g.NRT = (int32_t)cdiv_hd(d.blk, g.BM);
+  g.n_blocks = d.n_blocks;
+  g.n_split = 0;
+  g.grid = (int64_t)g.NG * d.n_blocks * g.NRT;
+  return g;
+}
+
+static inline WideGeom wide2_geom(const Dims& d, const Plan& p) {
+  WideGeom g{};
+  g.phase1 = 0;
+  g.HQ = d.HQ;
+  g.BM = kColsPerWave * d.RW;
+  g.NG = p.n_groups;
+  g.NRT = p.n_qtiles;
+  g.n_blocks = d.n_blocks;
+  g.n_split = p.n_split;
+  g.grid = (int64_t)g.NG * g.NRT * p.n_split;
+  return g;
+}
+
+// Wide kernel: workgroup bid -> (group gidx, work item). bid % NG keeps a
+// group on one XCD. With more groups than XCDs (several sequences, or head
+// sub-groups) each XCD runs its groups one after another, so its L2 holds
+// one group's K/V at a time. In phase 2, where the head sub-groups and query
+// tiles of a kv head read the same split, an XCD takes every work item of a
+// kv head, with the readers of one split next to each other (so they run at
+// the same time).
+STAR_HD static inline void wide_map(int64_t bid, bool phase1, int32_t NG, int32_t HQ, int32_t NRT,
+                                    int32_t n_split, int32_t n_blocks, int32_t* gidx,
+                                    int64_t* work) {
+  if (!phase1 && HQ * NRT > 1 && (NG / HQ) % kXcds == 0) {
+    const int64_t per_kv = (int64_t)HQ * NRT * n_split;
+    const int64_t i = bid / kXcds, r = i % per_kv;
+    *gidx = ((int32_t)(bid % kXcds) + kXcds * (int32_t)(i / per_kv)) * HQ + (int32_t)(r % HQ);
+    *work = r / HQ;
+  } else if (NG > kXcds && NG % kXcds == 0) {
+    const int64_t per_group = phase1 ? (int64_t)n_blocks * NRT : (int64_t)NRT * n_split;
+    const int64_t i = bid / kXcds;
+    *gidx = (int32_t)(bid % kXcds) + kXcds * (int32_t)(i / per_group);
+    *work = i % per_group;
+  } else {
+    *gidx = (int32_t)(bid % NG);
+    *work = bid / NG;
+  }
+}
+
+// Phase 1: work item -> (block i, row tile rt). Anchored blocks go first, one
+// after another, each by descending row tile (the heaviest first), then
+// block 0: the workgroups an XCD runs at once are neighbouring row tiles of
+// one block and share the anchor's and the block's K/V tiles in its L2.
+STAR_HD static inline void phase1_item(int64_t work, int32_t n_blocks, int32_t NRT, int64_t* i,
+                                       int64_t* rt) {
+  const int64_t n1 = (int64_t)(n_blocks - 1) * NRT;
+  if (work < n1) {
+    *rt = NRT - 1 - work % NRT;
+    *i = 1 + work / NRT;
+  } else {
+    *rt = NRT - 1 - (work - n1);
+    *i = 0;
+  }
+}
+
+// The 64-key tiles one workgroup reads. Anchor keys [0, hiA): interior tiles
+// [0, nAi), plus edge tile nAi when hiA is not a multiple of 64. Block keys
+// [loB, hiB), causal: interior tiles [i0, i1), whose 64 keys all lie in
+// [loB, hiB) at or before min_pos (the earliest query position of the
+// workgroup), so every column sees them unmasked; edge tiles [bf, i0) and
+// [i1, bl), masked per key.
+struct TileRuns {
+  int64_t nAi, bf, bl, i0, i1;
+  int32_t a_edge;
+};
+
+STAR_HD static inline TileRuns tile_runs(int64_t hiA, int64_t loB, int64_t hiB, int64_t min_pos) {
+  TileRuns t{};
+  t.nAi = hiA / 64;
+  t.a_edge = (hiA % 64) != 0;
+  if (hiB > loB) {
+    t.bf = loB / 64;
+    t.bl = cdiv_hd(hiB, 64);
+    int64_t t1 = hiB / 64;
+    const int64_t tp = (min_pos + 1) / 64;
+    if (tp < t1) t1 = tp;
+    const int64_t t0 = cdiv_hd(loB, 64);
+    t.i0 = t0 > t.bf ? t0 : t.bf;
+    t.i1 = t1 < t.bl ? t1 : t.bl;
+    if (t.i1 < t.i0) t.i1 = t.i0;
+  }
+  return t;
+}
+
+// Wide kernel, wave w of a workgroup -> its first query row (relative to the
+// workgroup's first row) and the head hw (of the HW heads of the workgroup)
+// of its 32*QT columns: WPR = 2/QT waves share one 64-row sub-tile of one head.
+STAR_HD static inline void wide_wave(int w, int QT, int HW, int* hw, int64_t* row_off) {
+  const int WPR = 2 / QT;
+  const int wsub = w % WPR, wh = w / WPR;  // 32*QT-row piece, (head, 64-row sub-tile)
+  *hw = wh % HW;
+  *row_off = (int64_t)(wh / HW) * 64 + wsub * 32 * QT;
+}
+
+// Decode kernel (balanced plan): four waves per workgroup, one range each;
+// WPG workgroups per (sequence, kv head) group.
+static inline int64_t decode_grid(const Dims& d, const Plan& p, int32_t* wpg) {
+  *wpg = (p.n_wg + 3) / 4;
+  return (int64_t)d.B * d.Hkv * *wpg;
+}
+
+// Workgroup bid, wave w -> group gidx and range r (r >= n_wg: no range, the
+// wave exits). The workgroups holding the last ranges (the tail and the
+// appended rows) start first.
+STAR_HD static inline void decode_map(int64_t bid, int w, int32_t NG, int32_t WPG, int32_t* gidx,
+                                      int64_t* r) {
+  *gidx = (int32_t)(bid % NG);
+  *r = (int64_t)(WPG - 1 - (int32_t)(bid / NG)) * 4 + w;
+}
+
+// Range r of the balanced plan: rows [lo, hi), the host boundary bnd inside
+// it (or -1), its first split sigma (sigma + 1 starts at bnd), its 32-key
+// slices n_sl, and n_in, the leading slices every query column sees whole.
+struct DecodeRange {
+  int64_t lo, hi, bnd;
+  int32_t sigma, n_sl, n_in;
+};
+
+STAR_HD static inline DecodeRange decode_range(int64_t r, int64_t wg_rows, int64_t kv_len, int64_t L,
+                                               int64_t blk, int32_t n_blocks, int64_t bnd_period,
+                                               int64_t pos0) {
+  DecodeRange d{};
+  d.lo = r * wg_rows;
+  d.hi = d.lo + wg_rows < kv_len ? d.lo + wg_rows : kv_len;
+  d.bnd = inner_boundary(L, blk, n_blocks, d.lo, d.hi);
+  d.sigma = (int32_t)(r + inner_boundaries_below(L, blk, n_blocks, wg_rows, bnd_period, d.lo));
+  d.n_sl = (int32_t)((d.hi - d.lo + 31) / 32);
+  const int64_t vis = pos0 + 1 < d.hi ? pos0 + 1 : d.hi;
+  d.n_in = vis > d.lo ? (int32_t)((vis - d.lo) / 32) : 0;
+  return d;
+}
+
+// Narrow kernel (blockwise plan): workgroup bid -> group gidx and split
+// sigma, splits in reverse order (the short, partly masked tail splits start
+// first).
+STAR_HD static inline void narrow_map(int64_t bid, int32_t NG, int32_t n_split, int32_t* gidx,
+                                      int32_t* sigma) {
+  *gidx = (int32_t)(bid % NG);
+  *sigma = n_split - 1 - (int32_t)(bid / NG);
+}
+
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
 // table / maxp: a paged cache (kc, vc the page pools; table [B][maxp] page
 // ids), or null / 0 for the contiguous cache.

@@ -71,7 +71,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // K-tile slot -> key offset inside a 32-key slice (bits 2 and 3 swapped).
 __device__ __forceinline__ int swap23(int x) {
@@ -359,7 +358,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 // accumulators are rescaled (by exp2((m_old - m_new) * c2)) only then; the
 // final O / l uses the same m, so the result is unchanged.
 constexpr float kTau = 8.0f;
-constexpr int kXcds = 8;  // MI355X: accelerator complex dies, one L2 each
 constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -667,60 +665,28 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
-  constexpr int WPR = 2 / QT;  // waves per 64-row sub-tile of one head
   static_assert(NW * QT == 8, "workgroup covers 256 columns");
   __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
   // the wave index is uniform: keep it (and what derives from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  // ---- which (group, work item) this workgroup is. Workgroups go to the
-  // XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2.
-  // bid % NG keeps a group on one XCD; with more groups than XCDs (several
-  // sequences, or query-head sub-groups) each XCD also runs its groups one
-  // after another, so its L2 holds one group's K/V at a time. In phase 2,
-  // where the query-head sub-groups and query tiles of a kv head read the
-  // same split, an XCD takes every work item of a kv head, with the readers
-  // of one split next to each other (so they run at the same time).
-  const int64_t bid = blockIdx.x;
-  int gidx;
+  // ---- which (group, work item) this workgroup is (XCD-aware order)
+  int32_t gidx;
   int64_t work;
-  if (!PHASE1 && a.HQ * a.NRT > 1 && (a.NG / a.HQ) % kXcds == 0) {
-    const int64_t per_kv = (int64_t)a.HQ * a.NRT * a.n_split;
-    const int64_t i = bid / kXcds, r = i % per_kv;
-    gidx = ((int)(bid % kXcds) + kXcds * (int)(i / per_kv)) * a.HQ + (int)(r % a.HQ);
-    work = r / a.HQ;
-  } else if (a.NG > kXcds && a.NG % kXcds == 0) {
-    const int64_t per_group = PHASE1 ? (int64_t)a.n_blocks * a.NRT : (int64_t)a.NRT * a.n_split;
-    const int64_t i = bid / kXcds;
-    gidx = (int)(bid % kXcds) + kXcds * (int)(i / per_group);
-    work = i % per_group;
-  } else {
-    gidx = (int)(bid % a.NG);
-    work = bid / a.NG;
-  }
+  wide_map(blockIdx.x, PHASE1, a.NG, a.HQ, a.NRT, a.n_split, a.n_blocks, &gidx, &work);
   const int hq = gidx % a.HQ, t2 = gidx / a.HQ;
   const int kvh = t2 % a.Hkv, s = t2 / a.Hkv;
-  const int wsub = w % WPR, wh = w / WPR;  // 32*QT-row piece, (head, 64-row sub-tile)
-  const int hw = wh % a.HW, rw = wh / a.HW;
+  int hw;
+  int64_t wrow_off;  // this wave's first query row, from the workgroup's
+  wide_wave(w, QT, a.HW, &hw, &wrow_off);
   const int head = kvh * a.G + hq * a.HW + hw;
 
   int64_t row0, row_end, hiA = 0, loB, hiB, pos_off;
   int32_t sigma = 0;
   if (PHASE1) {
-    // anchored blocks one after another, each by descending row tile (the
-    // heaviest first), then block 0: the workgroups that an XCD runs at once
-    // are neighbouring row tiles of one block, and share the anchor's and
-    // the block's K/V tiles in its L2
-    const int64_t n1 = (int64_t)(a.n_blocks - 1) * a.NRT;
     int64_t i, rt;
-    if (work < n1) {
-      rt = a.NRT - 1 - work % a.NRT;
-      i = 1 + work / a.NRT;
-    } else {
-      rt = a.NRT - 1 - (work - n1);
-      i = 0;
-    }
+    phase1_item(work, a.n_blocks, a.NRT, &i, &rt);
     row0 = i * a.blk + rt * a.BM;
     row_end = (i + 1) * a.blk < a.L ? (i + 1) * a.blk : a.L;
     if (row0 >= row_end) return;
@@ -739,7 +705,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
                &hiB, &host);
     pos_off = a.kv_len - a.q_tokens;
   }
-  const int64_t wrow0 = row0 + rw * 64 + wsub * 32 * QT;  // this wave's first query row
+  const int64_t wrow0 = row0 + wrow_off;  // this wave's first query row
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
   const uint16_t* K = PAGED ? a.k : a.k + head_row0 * D;
   const uint16_t* V = PAGED ? a.v : a.v + head_row0 * D;
@@ -796,21 +762,10 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
 
   // ---- tile classes. Range A: anchor [0, hiA), no mask. Range B: [loB, hiB),
   // causal (key <= query position). Interior tiles need no mask at all.
-  const int64_t min_pos = row0 + pos_off;
-  const int nAi = (int)(hiA / 64);
-  const bool a_edge = (hiA % 64) != 0;
-  int64_t bf = 0, bl = 0, i0 = 0, i1 = 0;
-  if (hiB > loB) {
-    bf = loB / 64;
-    bl = cdiv64(hiB, 64);
-    int64_t t1 = hiB / 64;
-    const int64_t tp = (min_pos + 1) / 64;
-    if (tp < t1) t1 = tp;
-    const int64_t t0 = cdiv64(loB, 64);
-    i0 = t0 > bf ? t0 : bf;
-    i1 = t1 < bl ? t1 : bl;
-    if (i1 < i0) i1 = i0;
-  }
+  const TileRuns runs = tile_runs(hiA, loB, hiB, row0 + pos_off);
+  const int nAi = (int)runs.nAi;
+  const bool a_edge = runs.a_edge != 0;
+  const int64_t bf = runs.bf, bl = runs.bl, i0 = runs.i0, i1 = runs.i1;
   const int n_int = nAi + (int)(i1 - i0);
   // interior tiles j0 .. j0 + cnt - 1 (anchor tiles first, then the block's);
   // tile j of the run -> byte offset of its rows (clamped to the last tile)
@@ -1063,8 +1018,8 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
 
   // splits in reverse order: the short, partly masked tail splits start
   // first instead of waiting for a CU after the long context splits
-  const int gidx = (int)(blockIdx.x % a.NG);
-  const int32_t sigma = a.n_split - 1 - (int32_t)(blockIdx.x / a.NG);
+  int32_t gidx, sigma;
+  narrow_map(blockIdx.x, a.NG, a.n_split, &gidx, &sigma);
   const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
   int64_t lo, hi;
   int32_t host;
@@ -1129,18 +1084,8 @@ __global__ __launch_bounds__(256) void attn_narrow_kernel(const NarrowArgs a) {
   };
 
   // interior tiles: inside [lo, hi) and not after any query position
-  int64_t bf = 0, bl = 0, i0 = 0, i1 = 0;
-  if (hi > lo) {
-    bf = lo / 64;
-    bl = cdiv64(hi, 64);
-    int64_t t1 = hi / 64;
-    const int64_t tpz = (pos0 + 1) / 64;
-    if (tpz < t1) t1 = tpz;
-    const int64_t t0 = cdiv64(lo, 64);
-    i0 = t0 > bf ? t0 : bf;
-    i1 = t1 < bl ? t1 : bl;
-    if (i1 < i0) i1 = i0;
-  }
+  const TileRuns runs = tile_runs(0, lo, hi, pos0);
+  const int64_t bf = runs.bf, bl = runs.bl, i0 = runs.i0, i1 = runs.i1;
   const int n_int = (int)(i1 - i0);
 
   if (n_int > 0) {
@@ -1352,17 +1297,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   char* qsm = ring + 2 * Dg::SB;    // and its query tile
 
   // the workgroup holding the last ranges (the tail, the appended rows) first
-  const int gidx = (int)(blockIdx.x % a.NG);
-  const int64_t r = (int64_t)(a.WPG - 1 - (int32_t)(blockIdx.x / a.NG)) * 4 + w;
+  int32_t gidx;
+  int64_t r;
+  decode_map(blockIdx.x, w, a.NG, a.WPG, &gidx, &r);
   if (r >= a.n_wg) return;
   const int kvh = gidx % a.Hkv, s = gidx / a.Hkv;
-  const int64_t lo = r * a.wg_rows;
-  const int64_t hi = lo + a.wg_rows < a.kv_len ? lo + a.wg_rows : a.kv_len;
-  // split sigma from lo; with a host boundary bnd inside, split sigma + 1 from bnd
-  const int64_t bnd = inner_boundary(a.L, a.blk, a.n_blocks, lo, hi);
-  const int32_t sigma =
-      (int32_t)(r + inner_boundaries_below(a.L, a.blk, a.n_blocks, a.wg_rows, a.bnd_period, lo));
   const int64_t pos0 = a.kv_len - a.n_query;
+  // split sigma from lo; with a host boundary bnd inside, split sigma + 1 from bnd
+  const DecodeRange rg =
+      decode_range(r, a.wg_rows, a.kv_len, a.L, a.blk, a.n_blocks, a.bnd_period, pos0);
+  const int64_t lo = rg.lo, hi = rg.hi, bnd = rg.bnd;
+  const int32_t sigma = rg.sigma;
   const int ncols = (int)(a.n_query * a.G);
   const int cj = l32 / a.G, ch = kvh * a.G + l32 % a.G;  // column l32 -> (query, head)
   const bool cvalid = l32 < ncols;
@@ -1428,9 +1373,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   // slices of [lo, hi): [0, n_in) fully visible to every column and inside
   // [lo, hi); [n_in, n_sl) masked (range end not on a slice, or keys after
   // the first query position)
-  const int n_sl = (int)((hi - lo + 31) / 32);
-  int64_t vis = pos0 + 1 < hi ? pos0 + 1 : hi;
-  const int n_in = vis > lo ? (int)((vis - lo) / 32) : 0;
+  const int n_sl = rg.n_sl;
+  const int n_in = rg.n_in;
   // split 2 starts in slice sb; if bnd is not on a slice edge, that slice's
   // keys below bnd still belong to split 1
   const int sb = bnd >= 0 ? (int)((bnd - lo) / 32) : 0x7fffffff;
@@ -1860,9 +1804,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
 
-// Waves per wide-kernel workgroup: 8, two per SIMD, 32 columns each (four
-// waves of 64 columns need more than the 512 registers of a lane and spill).
-constexpr int kWideWaves = 8;
+// kWideWaves (8 waves per wide-kernel workgroup): two per SIMD, 32 columns
+// each (four waves of 64 columns need more than the 512 registers of a lane
+// and spill).
 
 }  // namespace
 
@@ -1972,18 +1916,18 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
   a.G = d.G;
+  const WideGeom gm = phase1_geom(d);
   a.HW = d.HW;
-  a.HQ = d.HQ;
-  a.BM = kColsPerWave * d.RW;
-  a.NG = d.B * d.Hkv * d.HQ;
-  a.NRT = (int32_t)((d.blk + a.BM - 1) / a.BM);
+  a.HQ = gm.HQ;
+  a.BM = gm.BM;
+  a.NG = gm.NG;
+  a.NRT = gm.NRT;
   a.scale = d.scale;
   a.c2 = d.scale_log2;
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
-  const int64_t nwg = (int64_t)a.NG * d.n_blocks * a.NRT;
-  if (!grid_fits(nwg, 64 * kWideWaves)) return STAR_ERR_SHAPE;
-  const dim3 grid((unsigned)nwg);
+  if (!grid_fits(gm.grid, 64 * kWideWaves)) return STAR_ERR_SHAPE;
+  const dim3 grid((unsigned)gm.grid);
   if (d.D == 128)
     hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, true, false, ROPE, false>), grid,
                        dim3(64 * kWideWaves), 0, st, a);
@@ -2024,7 +1968,7 @@ static DecodeArgs decode_args(const Dims& d, const Plan& p, const void* kc, cons
   a.Hkv = d.Hkv;
   a.G = d.G;
   a.NG = d.B * d.Hkv;
-  a.WPG = (p.n_wg + 3) / 4;
+  (void)decode_grid(d, p, &a.WPG);
   a.scale = d.scale;
   a.c2 = d.scale_log2;
   return a;
@@ -2129,16 +2073,17 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
   a.G = d.G;
+  const WideGeom gm = wide2_geom(d, p);
   a.HW = d.HW;
-  a.HQ = d.HQ;
-  a.BM = kColsPerWave * d.RW;
-  a.NG = p.n_groups;
-  a.NRT = p.n_qtiles;
+  a.HQ = gm.HQ;
+  a.BM = gm.BM;
+  a.NG = gm.NG;
+  a.NRT = gm.NRT;
   a.scale = d.scale;
   a.c2 = d.scale_log2;
   a.pm = pm;
-  if (!grid_fits((int64_t)a.NG * a.NRT * p.n_split, 64 * kWideWaves)) return STAR_ERR_SHAPE;
-  const dim3 grid((unsigned)((int64_t)a.NG * a.NRT * p.n_split));
+  if (!grid_fits(gm.grid, 64 * kWideWaves)) return STAR_ERR_SHAPE;
+  const dim3 grid((unsigned)gm.grid);
   // one reader per split: a non-temporal stream; several: L2 serves the rest
   const bool kv_nt = a.HQ * a.NRT == 1;
   if (d.D == 128 && kv_nt)

@@ -1,16 +1,19 @@
-"""Runs the hot path through the C ABI on the GPU for a synthetic workload.
+"""A synthetic workload resident on the GPU, driven through the C ABI.
 
-Shared by the GPU parity tests, the smoke check and the bench: inputs come
-from the seeded generator, every step is a call of libstarattn through the
-Python binding, torch only allocates device memory.
+``Pipeline`` holds one workload's inputs, KV cache and outputs in device
+memory and runs each step of the path as one call of libstarattn through
+the Python binding: the context KV write, phase 1, the query step and the
+decode steps. It only allocates device tensors and marshals arguments;
+every arithmetic step runs in the HIP kernels. The bench, the smoke check
+and the GPU tests all drive the path through it.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-import long_context_attention_phase1_amd as sa
-from long_context_attention_phase1_amd import synthetic as syn
+from . import binding as sa
+from . import synthetic as syn
 
 NAN_BF16 = 0x7FC0
 
@@ -165,7 +168,7 @@ class PagedPipeline(Pipeline):
     def __init__(self, w: syn.Workload, inputs=None, device="cuda", fill_nan=True, threads=None,
                  spare=5, table_seed=7):
         super().__init__(w, inputs=inputs, device=device, fill_nan=fill_nan, threads=threads)
-        self.maxp = -(-(w.ctx_len + w.tail_cap) // sa.binding.STAR_KV_TILE)
+        self.maxp = -(-(w.ctx_len + w.tail_cap) // sa.STAR_KV_TILE)
         self.n_pages = w.batch * self.maxp + spare
         self.k_pages = sa.alloc_kv_pages(self.desc, self.n_pages, device)
         self.v_pages = sa.alloc_kv_pages(self.desc, self.n_pages, device)

@@ -18,7 +18,7 @@ import torch
 import long_context_attention_phase1_amd as sa
 from long_context_attention_phase1_amd import synthetic as syn
 from oracle import star_oracle as orc
-from tests.gpu_pipeline import Pipeline, to_host_f64
+from long_context_attention_phase1_amd.pipeline import Pipeline, to_host_f64
 
 pytestmark = pytest.mark.gpu
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from long_context_attention_phase1_amd import synthetic as syn
-from tests.gpu_pipeline import Pipeline
+from long_context_attention_phase1_amd.pipeline import Pipeline
 
 pytestmark = pytest.mark.gpu
 
