@@ -27,6 +27,8 @@ int validate_desc(const star_attn_desc* d, Dims* out) {
   const int64_t rows = round_up(d->ctx_len + d->tail_cap, kTile);
   if (rows > ((int64_t)1 << 40) || (int64_t)d->batch * d->n_q_heads > (1 << 24))
     return STAR_ERR_SHAPE;
+  // block indices are 32-bit
+  if (cdiv(d->ctx_len, d->block_len) > INT32_MAX) return STAR_ERR_SHAPE;
   if (out) {
     Dims& o = *out;
     o.B = d->batch;
@@ -124,10 +126,26 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
   const int64_t tail = kv_len - d.L;
   const int64_t tl_target =
       p.per_block > 1 ? p.blk_len : (d.blk > min_len ? round_up(d.blk, kTile) : min_len);
-  p.tail_splits = (int32_t)cdiv(tail, tl_target);
+  const int64_t tail_splits = cdiv(tail, tl_target);
+  const int64_t n_split = (int64_t)d.n_blocks * p.per_block + tail_splits;
+  if (n_split > INT32_MAX) {  // split ids are 32-bit: the caller refuses the shape
+    p.n_split = 0;
+    return p;
+  }
+  p.tail_splits = (int32_t)tail_splits;
   p.tail_len = p.tail_splits == 1 ? tail : round_up(cdiv(tail, p.tail_splits), kTile);
-  p.n_split = d.n_blocks * p.per_block + p.tail_splits;
+  p.n_split = (int32_t)n_split;
   return p;
+}
+
+// Every grid of a decode step (the append, the partials, the merge), checked
+// before the first launch so that a call that fails writes nothing.
+static int decode_step_fits(const Dims& d, const Plan& p, int64_t kv_len, int64_t n_query) {
+  if (p.n_split < 1 || !partial_fits(d, p, n_query) || !merge_fits(d, n_query))
+    return STAR_ERR_SHAPE;
+  const bool fused = p.narrow && d.dtype == STAR_BF16;
+  if (!fused && !grid_fits(kv_write_grid(d, kv_len - n_query, n_query), 256)) return STAR_ERR_SHAPE;
+  return STAR_OK;
 }
 
 }  // namespace star
@@ -150,6 +168,7 @@ int star_kv_write(const star_attn_desc* desc, void* k_cache, void* v_cache, int6
   if (st) return st;
   if (!k_cache || !v_cache || !k_src || !v_src || n_tok < 1) return STAR_ERR_INVALID_ARG;
   if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  if (!grid_fits(kv_write_grid(d, pos0, n_tok), 256)) return STAR_ERR_SHAPE;
   return launch_kv_write(d, k_cache, v_cache, pos0, k_src, v_src, n_tok, stream);
 }
 
@@ -159,6 +178,7 @@ int star_attn_phase1(const star_attn_desc* desc, const void* k_cache, const void
   int st = validate_desc(desc, &d);
   if (st) return st;
   if (!k_cache || !v_cache || !q_ctx || !o_ctx) return STAR_ERR_INVALID_ARG;
+  if (!phase1_fits(d)) return STAR_ERR_SHAPE;
   return launch_phase1(d, k_cache, v_cache, q_ctx, o_ctx, stream);
 }
 
@@ -170,7 +190,9 @@ int star_attn_phase2_plan(const star_attn_desc* desc, int64_t kv_len, int64_t n_
   if (!n_split) return STAR_ERR_INVALID_ARG;
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
-  *n_split = make_plan(d, kv_len, n_query).n_split;
+  const Plan p = make_plan(d, kv_len, n_query);
+  if (p.n_split < 1) return STAR_ERR_SHAPE;
+  *n_split = p.n_split;
   return STAR_OK;
 }
 
@@ -183,7 +205,7 @@ int star_attn_phase2_split_range(const star_attn_desc* desc, int64_t kv_len, int
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
   const Plan p = make_plan(d, kv_len, n_query);
-  if (split < 0 || split >= p.n_split) return STAR_ERR_SHAPE;
+  if (p.n_split < 1 || split < 0 || split >= p.n_split) return STAR_ERR_SHAPE;
   split_range(d, p, kv_len, split, lo, hi, host);
   return STAR_OK;
 }
@@ -198,6 +220,7 @@ int star_attn_phase2_partial(const star_attn_desc* desc, const void* k_cache, co
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
   const Plan p = make_plan(d, kv_len, n_query);
+  if (p.n_split < 1 || !partial_fits(d, p, n_query)) return STAR_ERR_SHAPE;
   return launch_phase2_partial(d, p, k_cache, v_cache, kv_len, q, n_query, o_part, lse_part,
                                stream);
 }
@@ -211,6 +234,7 @@ int star_attn_lse_merge(const star_attn_desc* desc, int64_t n_query, int32_t n_s
   if (!o_part || !lse_part || !o || n_query < 1 || n_split < 1) return STAR_ERR_INVALID_ARG;
   if (o_dtype != STAR_BF16 && o_dtype != STAR_F32) return STAR_ERR_DTYPE;
   if (n_query > d.tail_cap) return STAR_ERR_SHAPE;
+  if (!merge_fits(d, n_query)) return STAR_ERR_SHAPE;
   return launch_lse_merge(d, n_query, n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }
 
@@ -227,6 +251,8 @@ int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cac
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
   const Plan p = make_plan(d, kv_len, n_query);
+  st = decode_step_fits(d, p, kv_len, n_query);
+  if (st) return st;
   if (p.narrow && d.dtype == STAR_BF16)
     return launch_decode_step(d, p, k_cache, v_cache, kv_len, q, k_new, v_new, n_query, o_part,
                               lse_part, o, o_dtype, lse_out, stream);
@@ -266,6 +292,7 @@ int star_kv_write_paged(const star_attn_desc* desc, void* k_pages, void* v_pages
   st = validate_pages(d, k_pages, v_pages, block_table, max_pages);
   if (st) return st;
   if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  if (!grid_fits(kv_write_grid(d, pos0, n_tok), 256)) return STAR_ERR_SHAPE;
   return launch_kv_write(d, k_pages, v_pages, pos0, k_src, v_src, n_tok, stream, block_table,
                          max_pages);
 }
@@ -283,6 +310,7 @@ int star_attn_phase2_partial_paged(const star_attn_desc* desc, const void* k_pag
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
   const Plan p = make_plan(d, kv_len, n_query);
+  if (p.n_split < 1 || !partial_fits(d, p, n_query)) return STAR_ERR_SHAPE;
   return launch_phase2_partial(d, p, k_pages, v_pages, kv_len, q, n_query, o_part, lse_part,
                                stream, block_table, max_pages);
 }
@@ -302,6 +330,8 @@ int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void*
   st = validate_phase2(d, kv_len, n_query);
   if (st) return st;
   const Plan p = make_plan(d, kv_len, n_query);
+  st = decode_step_fits(d, p, kv_len, n_query);
+  if (st) return st;
   if (p.narrow && d.dtype == STAR_BF16)
     return launch_decode_step(d, p, k_pages, v_pages, kv_len, q, k_new, v_new, n_query, o_part,
                               lse_part, o, o_dtype, lse_out, stream, block_table, max_pages);
@@ -334,6 +364,7 @@ int star_kv_write_rope(const star_attn_desc* desc, void* k_cache, void* v_cache,
   st = validate_rope(d, rope);
   if (st) return st;
   if (pos0 < 0 || pos0 + n_tok > d.L + d.tail_cap) return STAR_ERR_SHAPE;
+  if (!grid_fits(kv_write_grid(d, pos0, n_tok), 256)) return STAR_ERR_SHAPE;
   return launch_kv_write(d, k_cache, v_cache, pos0, k_src, v_src, n_tok, stream, nullptr, 0,
                          rope->cos, rope->sin);
 }
@@ -346,6 +377,7 @@ int star_attn_phase1_rope(const star_attn_desc* desc, const void* k_cache, const
   if (!k_cache || !v_cache || !q_ctx || !o_ctx) return STAR_ERR_INVALID_ARG;
   st = validate_rope(d, rope);
   if (st) return st;
+  if (!phase1_fits(d)) return STAR_ERR_SHAPE;
   return launch_phase1(d, k_cache, v_cache, q_ctx, o_ctx, stream, rope->cos, rope->sin,
                        rope->anchor_mode);
 }

@@ -319,6 +319,43 @@ STAR_HD static inline void narrow_map(int64_t bid, int32_t NG, int32_t n_split, 
   *sigma = n_split - 1 - (int32_t)(bid / NG);
 }
 
+// ---- grid sizes of every launch, checked before a call enqueues anything
+//
+// HIP takes a grid as a 32-bit count of work-items: a launch whose
+// workgroups would not fit is refused (STAR_ERR_SHAPE) rather than
+// truncated. The entry points check every grid of a call before its first
+// launch, so a call that fails writes nothing.
+static inline bool grid_fits(int64_t wgs, int threads) {
+  return wgs >= 1 && wgs <= (int64_t)0xFFFFFFFF / threads;
+}
+
+// kv_write: one 256-thread workgroup per (64-row tile touched, sequence, kv head)
+static inline int64_t kv_write_grid(const Dims& d, int64_t pos0, int64_t n_tok) {
+  return ((pos0 + n_tok - 1) / kTile - pos0 / kTile + 1) * d.B * d.Hkv;
+}
+
+// phase 1: bf16 wide kernel (512 threads), or one wave per column (fp32)
+static inline bool phase1_fits(const Dims& d) {
+  if (d.dtype == STAR_F32) return grid_fits(((int64_t)d.B * d.L * d.Hq + 3) / 4, 256);
+  return grid_fits(phase1_geom(d).grid, 64 * kWideWaves);
+}
+
+// phase-2 partials under plan p
+static inline bool partial_fits(const Dims& d, const Plan& p, int64_t n_query) {
+  if (d.dtype == STAR_F32) return grid_fits(((int64_t)d.B * n_query * d.Hq * p.n_split + 3) / 4, 256);
+  if (p.narrow && p.balanced) {
+    int32_t wpg;
+    return grid_fits(decode_grid(d, p, &wpg), 256);
+  }
+  if (p.narrow) return grid_fits((int64_t)d.B * d.Hkv * p.n_split, 256);
+  return grid_fits(wide2_geom(d, p).grid, 64 * kWideWaves);
+}
+
+// the merge: one workgroup per (sequence, query, head) row
+static inline bool merge_fits(const Dims& d, int64_t n_query) {
+  return grid_fits((int64_t)d.B * n_query * d.Hq, 256);
+}
+
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
 // table / maxp: a paged cache (kc, vc the page pools; table [B][maxp] page
 // ids), or null / 0 for the contiguous cache.

@@ -1813,13 +1813,9 @@ int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-// HIP takes a grid as a 32-bit count of work-items: a launch whose
-// workgroups would not fit is refused (STAR_ERR_SHAPE) before anything is
-// enqueued, rather than truncated.
-static bool grid_fits(int64_t wgs, int threads) {
-  return wgs >= 1 && wgs <= (int64_t)0xFFFFFFFF / threads;
-}
-
+// Every launcher refuses a grid that does not fit HIP's 32-bit count of
+// work-items (grid_fits) with STAR_ERR_SHAPE before enqueueing it; the
+// entry points have already checked every grid of the call.
 template <bool PAGED, bool ROPE>
 static int kv_write_impl(const Dims& d, void* kc, void* vc, int64_t pos0, const void* ks,
                          const void* vs, int64_t n_tok, const PageMap& pm, const float* rope_cos,

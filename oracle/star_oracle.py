@@ -21,8 +21,8 @@ over Long Sequences"):
 * paperhub.cn rebuttal page: reply to reviewer EMsM, point 5, and reply to
   x5MA, point 1 (phase 1 attention is causal; the anchor is the first context
   block and is at most one block long); reply to dnhh, point 2 (phase 2 is
-  dense over the full KV cache built in phase 1); reply to dnhh, point 1 and
-  to dKGV, point 1 (no communication between hosts in phase 1).
+  dense over the full KV cache built in phase 1); replies to dnhh, points 1
+  and 3, and to dKGV, point 1 (no communication between hosts in phase 1).
 
 Readings where the pages are silent are listed with each function; the
 same list is kept with the project's design notes.

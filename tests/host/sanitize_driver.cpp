@@ -7,8 +7,9 @@
 // sequence), and the planner on thousands of seeded random shapes, checking
 // that the splits cover [0, kv_len) once, in order, each inside one host.
 // Built and run by tests/test_host_sanitizers.py; no GPU is involved.
-#include <cstdio>
 #include <cstdint>
+#include <cstdio>
+#include <initializer_list>
 
 #include "star_internal.hpp"
 
@@ -181,6 +182,43 @@ int main() {
   r.anchor_mode = 2;
   CHECK(star_attn_phase1_rope(&ok, P, P, P, &r, P, nullptr) == STAR_ERR_INVALID_ARG);
   CHECK(g_launches == before);
+
+  // ---- 32-bit block and split indices: a block count past INT32_MAX is refused
+  for (const int64_t L : {((int64_t)1 << 32) + 5, ((int64_t)1 << 31) + 1}) {
+    const star_attn_desc big = make(1, 1, 1, 128, L, 1, 1, 8, STAR_BF16);
+    int32_t n = -1;
+    before = g_launches;
+    CHECK(star_kv_cache_bytes(&big) == 0);
+    CHECK(star_attn_phase1(&big, P, P, P, P, nullptr) == STAR_ERR_SHAPE);
+    CHECK(star_attn_phase2_plan(&big, L + 1, 1, &n) == STAR_ERR_SHAPE && n == -1);
+    CHECK(star_attn_decode_step(&big, P, P, L + 1, P, P, P, 1, F, F, P, STAR_BF16, nullptr,
+                                nullptr) == STAR_ERR_SHAPE);
+    CHECK(g_launches == before);
+  }
+  // ---- every grid of a multi-launch call is checked before the first launch:
+  // 2^23 query heads, GQA 4:1, 8 query rows: the fused append + partials fit
+  // one grid, the merge (2^26 rows) does not, so nothing may be launched
+  {
+    const star_attn_desc wide = make(1, 1 << 23, 1 << 21, 128, 128, 128, 128, 16, STAR_BF16);
+    int32_t n = -1;
+    CHECK(star_attn_phase2_plan(&wide, 136, 8, &n) == STAR_OK && n >= 1);
+    before = g_launches;
+    CHECK(star_attn_decode_step(&wide, P, P, 136, P, P, P, 8, F, F, P, STAR_BF16, nullptr,
+                                nullptr) == STAR_ERR_SHAPE);
+    CHECK(star_attn_decode_step_paged(&wide, P, P, table, 4, 136, P, P, P, 8, F, F, P, STAR_BF16,
+                                      nullptr, nullptr) == STAR_ERR_SHAPE);
+    CHECK(star_attn_lse_merge(&wide, 8, n, F, F, P, STAR_BF16, nullptr, nullptr) ==
+          STAR_ERR_SHAPE);
+    // fp32: three launches (append, partials, merge), the merge too large
+    const star_attn_desc wide32 = make(1, 1 << 23, 1 << 21, 64, 128, 128, 128, 16, STAR_F32);
+    CHECK(star_attn_decode_step(&wide32, P, P, 136, P, P, P, 8, F, F, P, STAR_F32, nullptr,
+                                nullptr) == STAR_ERR_SHAPE);
+    CHECK(g_launches == before);
+    // one query row: every grid fits, the call launches
+    CHECK(star_attn_decode_step(&wide, P, P, 129, P, P, P, 1, F, F, P, STAR_BF16, nullptr,
+                                nullptr) == STAR_OK);
+    CHECK(g_launches > before);
+  }
 
   // ---- valid calls launch (the stubs count)
   r.anchor_mode = 1;

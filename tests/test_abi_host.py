@@ -93,6 +93,9 @@ BAD_DESCS = [
     (dict(head_dim=96), B.STAR_ERR_UNSUPPORTED),
     (dict(n_q_heads=30), B.STAR_ERR_SHAPE),
     (dict(anchor_len=16385), B.STAR_ERR_SHAPE),
+    # block indices are 32-bit: more than 2^31 - 1 blocks is refused
+    (dict(ctx_len=(1 << 32) + 5, block_len=1, anchor_len=1), B.STAR_ERR_SHAPE),
+    (dict(ctx_len=(1 << 31) + 1, block_len=1, anchor_len=1), B.STAR_ERR_SHAPE),
 ]
 
 
@@ -346,6 +349,25 @@ def test_launches_too_large_for_one_grid_are_refused_before_launching():
     tiny = _desc(ctx_len=1 << 28, block_len=1, anchor_len=1, tail_cap=64)
     assert lib.star_attn_phase2_partial(ctypes.byref(tiny), fake, fake, (1 << 28) + 64, fake, 64,
                                         fake, fake, None) == S
+
+
+def test_every_grid_of_a_decode_step_is_checked_before_the_first_launch():
+    """2^23 query heads (GQA 4:1) and 8 query rows: the fused append and
+    partials would fit one grid, the merge (2^26 rows) would not. The call is
+    refused before anything is enqueued (no GPU here: a call that reached a
+    launch would fail with STAR_ERR_HIP instead)."""
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(_desc(n_q_heads=1 << 23, n_kv_heads=1 << 21, ctx_len=128, block_len=128,
+                           anchor_len=128, tail_cap=16))
+    n = ctypes.c_int32()
+    assert lib.star_attn_phase2_plan(d, 136, 8, ctypes.byref(n)) == B.STAR_OK
+    assert lib.star_attn_decode_step(d, fake, fake, 136, fake, fake, fake, 8, fake, fake, fake,
+                                     B.STAR_BF16, None, None) == B.STAR_ERR_SHAPE
+    d32 = ctypes.byref(_desc(n_q_heads=1 << 23, n_kv_heads=1 << 21, head_dim=64, ctx_len=128,
+                             block_len=128, anchor_len=128, tail_cap=16, dtype=B.STAR_F32))
+    assert lib.star_attn_decode_step(d32, fake, fake, 136, fake, fake, fake, 8, fake, fake, fake,
+                                     B.STAR_F32, None, None) == B.STAR_ERR_SHAPE
 
 
 def test_binding_follows_the_header_abi_version():
