@@ -28,11 +28,13 @@
  *     no output byte is written.
  *   - Memory: every buffer is caller-owned device memory (except desc and the
  *     small host outputs such as n_split). The library never allocates, frees
- *     or synchronises. Buffers must be 16-byte aligned.
+ *     or synchronises; its one piece of device memory is the static scratch
+ *     array of star_attn_decode_step_noalloc. Buffers must be 16-byte aligned.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream). All work is
  *     enqueued asynchronously on it, in call order.
  *   - Thread safety: stateless and re-entrant; calls on different streams may
- *     run concurrently as long as they do not write the same buffers.
+ *     run concurrently as long as they do not write the same buffers
+ *     (star_attn_decode_step_noalloc writes its GPU's one scratch array).
  *   - Layouts are row-major C arrays; element types follow desc->dtype
  *     (bf16 = IEEE bfloat16 bit patterns, f32 = IEEE binary32) unless stated.
  */
@@ -293,6 +295,28 @@ int star_kv_write_rope(const star_attn_desc* desc, void* k_cache, void* v_cache,
  * ids). The cache holds K rotated at its rows (star_kv_write_rope). */
 int star_attn_phase1_rope(const star_attn_desc* desc, const void* k_cache, const void* v_cache,
                           const void* q_ctx, const star_rope* rope, void* o_ctx, void* stream);
+
+/*
+ * star_attn_decode_step_noalloc - star_attn_decode_step for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The same arguments less o_part and
+ * lse_part: the split partials live in a scratch array that the library
+ * holds in device memory, STAR_NOALLOC_SCRATCH_BYTES on each GPU it runs on,
+ * from the first call on that GPU until the process ends. The call allocates
+ * nothing, computes exactly what star_attn_decode_step computes (same kernels,
+ * same plan, bit-identical o and lse_out), and returns STAR_ERR_SHAPE when the
+ * partials do not fit the scratch (B * n_query * n_q_heads * n_split splits of
+ * head_dim + 1 floats each, the o part rounded up to 256 bytes). Every call on
+ * one GPU shares that GPU's scratch, which keeps the last call's partials:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * ordered by the caller. Returns STAR_ERR_HIP if the scratch's device address
+ * cannot be looked up on the current device.
+ */
+#define STAR_NOALLOC_SCRATCH_BYTES (16u << 20)
+int star_attn_decode_step_noalloc(const star_attn_desc* desc, void* k_cache, void* v_cache,
+                                  int64_t kv_len, const void* q, const void* k_new,
+                                  const void* v_new, int64_t n_query, void* o, int32_t o_dtype,
+                                  float* lse_out, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* star_attn_strerror(int status);

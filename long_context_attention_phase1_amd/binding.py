@@ -31,7 +31,7 @@ STAR_KV_TILE = 64
 
 EXPORTS = ("star_kv_cache_bytes", "star_kv_write", "star_attn_phase1", "star_attn_phase2_plan",
            "star_attn_phase2_split_range", "star_attn_phase2_partial", "star_attn_lse_merge",
-           "star_attn_decode_step", "star_kv_page_bytes", "star_kv_write_paged",
+           "star_attn_decode_step", "star_attn_decode_step_noalloc", "star_kv_page_bytes", "star_kv_write_paged",
            "star_attn_phase2_partial_paged", "star_attn_decode_step_paged", "star_kv_write_rope",
            "star_attn_phase1_rope", "star_attn_strerror", "star_attn_abi_version")
 
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "star_attn_phase2_partial": (ctypes.c_int, [D, P, P, I64, P, I64, P, P, P]),
         "star_attn_lse_merge": (ctypes.c_int, [D, I64, I32, P, P, P, I32, P, P]),
         "star_attn_decode_step": (ctypes.c_int, [D, P, P, I64, P, P, P, I64, P, P, P, I32, P, P]),
+        "star_attn_decode_step_noalloc": (ctypes.c_int, [D, P, P, I64, P, P, P, I64, P, I32, P, P]),
         "star_kv_page_bytes": (ctypes.c_size_t, [D]),
         "star_kv_write_rope": (ctypes.c_int, [D, P, P, I64, P, P, I64, ctypes.POINTER(StarRope), P]),
         "star_attn_phase1_rope": (ctypes.c_int, [D, P, P, P, ctypes.POINTER(StarRope), P, P]),
@@ -270,6 +271,27 @@ def star_attn_decode_step(desc, k_cache, v_cache, kv_len: int, q, k_new, v_new, 
         _ptr(v_new, shp_kv, elt, "v_new"), n_query, _ptr(o_part, shp_p, f32, "o_part"),
         _ptr(lse_part, shp_p[:4], f32, "lse_part"), _ptr(o, shp_q, od, "o"), o_dtype, _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
     _check(st, "star_attn_decode_step")
+
+
+STAR_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/star_attn.h
+
+
+def star_attn_decode_step_noalloc(desc, k_cache, v_cache, kv_len: int, q, k_new, v_new,
+                                  n_query: int, o, o_dtype: int, lse_out=None, stream=None):
+    """star_attn_decode_step with the split partials in the library's own
+    per-GPU scratch array (the call allocates nothing)."""
+    torch = None if isinstance(q, int) else _torch()
+    shp_q = (desc.batch, n_query, desc.n_q_heads, desc.head_dim)
+    shp_kv = (desc.batch, n_query, desc.n_kv_heads, desc.head_dim)
+    f32 = None if torch is None else torch.float32
+    elt = None if torch is None else _elt(desc)
+    od = None if torch is None else (torch.bfloat16 if o_dtype == STAR_BF16 else torch.float32)
+    st = load_library().star_attn_decode_step_noalloc(
+        ctypes.byref(desc), _cache_ptr(desc, k_cache, "k_cache"), _cache_ptr(desc, v_cache, "v_cache"),
+        kv_len, _ptr(q, shp_q, elt, "q"), _ptr(k_new, shp_kv, elt, "k_new"),
+        _ptr(v_new, shp_kv, elt, "v_new"), n_query, _ptr(o, shp_q, od, "o"), o_dtype,
+        _ptr(lse_out, shp_q[:3], f32, "lse_out"), _stream(stream))
+    _check(st, "star_attn_decode_step_noalloc")
 
 
 # ---------------------------------------------------------------- paged cache

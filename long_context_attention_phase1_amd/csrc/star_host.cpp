@@ -264,6 +264,37 @@ int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cac
   return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
 }
 
+int star_attn_decode_step_noalloc(const star_attn_desc* desc, void* k_cache, void* v_cache,
+                                  int64_t kv_len, const void* q, const void* k_new,
+                                  const void* v_new, int64_t n_query, void* o, int32_t o_dtype,
+                                  float* lse_out, void* stream) {
+  Dims d;
+  int st = validate_desc(desc, &d);
+  if (st) return st;
+  if (!k_cache || !v_cache || !q || !k_new || !v_new || !o) return STAR_ERR_INVALID_ARG;
+  if (o_dtype != STAR_BF16 && o_dtype != STAR_F32) return STAR_ERR_DTYPE;
+  st = validate_phase2(d, kv_len, n_query);
+  if (st) return st;
+  const Plan p = make_plan(d, kv_len, n_query);
+  st = decode_step_fits(d, p, kv_len, n_query);
+  if (st) return st;
+  if (!noalloc_fits(d, p, n_query)) return STAR_ERR_SHAPE;
+  void* base = nullptr;
+  st = scratch_address(&base);
+  if (st) return st;
+  float* o_part = (float*)base;
+  float* lse_part = (float*)((char*)base + noalloc_lse_offset(d, p, n_query));
+  // the same launches as star_attn_decode_step, on the scratch partials
+  if (p.narrow && d.dtype == STAR_BF16)
+    return launch_decode_step(d, p, k_cache, v_cache, kv_len, q, k_new, v_new, n_query, o_part,
+                              lse_part, o, o_dtype, lse_out, stream);
+  st = launch_kv_write(d, k_cache, v_cache, kv_len - n_query, k_new, v_new, n_query, stream);
+  if (st) return st;
+  st = launch_phase2_partial(d, p, k_cache, v_cache, kv_len, q, n_query, o_part, lse_part, stream);
+  if (st) return st;
+  return launch_lse_merge(d, n_query, p.n_split, o_part, lse_part, o, o_dtype, lse_out, stream);
+}
+
 // ---- paged cache: the same entry points, the cache read and written through a
 // block table
 

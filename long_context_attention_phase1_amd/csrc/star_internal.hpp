@@ -356,6 +356,22 @@ static inline bool merge_fits(const Dims& d, int64_t n_query) {
   return grid_fits((int64_t)d.B * n_query * d.Hq, 256);
 }
 
+// ---- the no-allocation decode step's scratch: o_part ([rows][n_split][D]
+// fp32) at offset 0, lse_part ([rows][n_split] fp32) at the next 256-byte
+// boundary, rows = B * n_query * Hq.
+static inline int64_t noalloc_lse_offset(const Dims& d, const Plan& p, int64_t n_query) {
+  const int64_t o_bytes = (int64_t)d.B * n_query * d.Hq * p.n_split * d.D * 4;
+  return (o_bytes + 255) / 256 * 256;
+}
+static inline bool noalloc_fits(const Dims& d, const Plan& p, int64_t n_query) {
+  const int64_t lse_bytes = (int64_t)d.B * n_query * d.Hq * p.n_split * 4;
+  return noalloc_lse_offset(d, p, n_query) + lse_bytes <= (int64_t)STAR_NOALLOC_SCRATCH_BYTES;
+}
+
+// Device address of the current GPU's scratch (star_kernels.hip): looked up
+// once per device, then reused. STAR_OK, or STAR_ERR_HIP.
+int scratch_address(void** ptr);
+
 // Kernel launchers (star_kernels.hip). Each returns STAR_OK or STAR_ERR_HIP.
 // table / maxp: a paged cache (kc, vc the page pools; table [B][maxp] page
 // ids), or null / 0 for the contiguous cache.

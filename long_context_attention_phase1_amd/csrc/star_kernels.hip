@@ -30,6 +30,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "star_internal.hpp"
@@ -2185,6 +2186,34 @@ int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const floa
   if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, dim3(256), 0, st, a);
   return check_launch();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of star_attn_decode_step_noalloc: the split partials of one decode
+// step, in a file-scope device array that every GPU the library runs on holds
+// until the process ends. In host code `scratch` only names the symbol; its
+// device address on the current GPU comes from hipGetSymbolAddress, looked up
+// once per device (with that device current) and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[STAR_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; null until looked up
+}  // namespace
+
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return STAR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STAR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return STAR_OK;
 }
 
 }  // namespace star

@@ -41,6 +41,7 @@ int launch_decode_step(const Dims&, const Plan&, void*, void*, int64_t, const vo
                        const int32_t*, int32_t) { return STAR_ERR_HIP; }
 int launch_lse_merge(const Dims&, int64_t, int32_t, const float*, const float*, void*, int32_t,
                      float*, void*) { return STAR_ERR_HIP; }
+int scratch_address(void**) { return STAR_ERR_HIP; }
 }  // namespace star
 
 using namespace star;

@@ -41,6 +41,11 @@ int launch_lse_merge(const Dims&, int64_t, int32_t, const float*, const float*, 
   ++g_launches;
   return STAR_OK;
 }
+static char g_scratch[64];
+int scratch_address(void** ptr) {
+  *ptr = g_scratch;  // a fake device address: the stub launchers never touch it
+  return STAR_OK;
+}
 }  // namespace star
 
 static int g_fail = 0;
@@ -217,6 +222,30 @@ int main() {
     // one query row: every grid fits, the call launches
     CHECK(star_attn_decode_step(&wide, P, P, 129, P, P, P, 1, F, F, P, STAR_BF16, nullptr,
                                 nullptr) == STAR_OK);
+    CHECK(g_launches > before);
+  }
+
+  // ---- the no-allocation decode step: same checks, plus the scratch size
+  {
+    before = g_launches;
+    CHECK(star_attn_decode_step_noalloc(&ok, P, P, 1005, P, P, P, 1, P, 9, nullptr, nullptr) ==
+          STAR_ERR_DTYPE);
+    CHECK(star_attn_decode_step_noalloc(&ok, P, P, 1005, nullptr, P, P, 1, P, STAR_BF16, nullptr,
+                                        nullptr) == STAR_ERR_INVALID_ARG);
+    CHECK(star_attn_decode_step_noalloc(&ok, P, P, 1000, P, P, P, 1, P, STAR_BF16, nullptr,
+                                        nullptr) == STAR_ERR_SHAPE);
+    // 256 query rows x 64 heads x n_split partials of 129 floats: beyond 16 MiB
+    const star_attn_desc big = make(1, 64, 8, 128, 131072, 16384, 16384, 512, STAR_BF16);
+    int32_t n = 0;
+    CHECK(star_attn_phase2_plan(&big, 131072 + 256, 256, &n) == STAR_OK);
+    CHECK((int64_t)256 * 64 * n * 129 * 4 > (int64_t)STAR_NOALLOC_SCRATCH_BYTES);
+    CHECK(star_attn_decode_step_noalloc(&big, P, P, 131072 + 256, P, P, P, 256, P, STAR_BF16,
+                                        nullptr, nullptr) == STAR_ERR_SHAPE);
+    CHECK(g_launches == before);
+    CHECK(star_attn_decode_step_noalloc(&ok, P, P, 1005, P, P, P, 1, P, STAR_BF16, nullptr,
+                                        nullptr) == STAR_OK);
+    CHECK(star_attn_decode_step_noalloc(&big, P, P, 131072 + 1, P, P, P, 1, P, STAR_BF16, nullptr,
+                                        nullptr) == STAR_OK);
     CHECK(g_launches > before);
   }
 

@@ -370,8 +370,28 @@ def test_every_grid_of_a_decode_step_is_checked_before_the_first_launch():
                                      B.STAR_F32, None, None) == B.STAR_ERR_SHAPE
 
 
+def test_noalloc_decode_step_refuses_partials_beyond_its_scratch():
+    """star_attn_decode_step_noalloc keeps its partials in a fixed device
+    array: a plan whose partials do not fit is STAR_ERR_SHAPE before any HIP
+    call (no GPU here; a fitting shape reaches the runtime and reports
+    STAR_ERR_HIP instead)."""
+    lib = sa.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    d = _desc(n_q_heads=64, tail_cap=512)
+    n = ctypes.c_int32()
+    kv = 131072 + 256
+    assert lib.star_attn_phase2_plan(ctypes.byref(d), kv, 256, ctypes.byref(n)) == B.STAR_OK
+    assert 256 * 64 * n.value * 129 * 4 > B.STAR_NOALLOC_SCRATCH_BYTES
+    assert lib.star_attn_decode_step_noalloc(ctypes.byref(d), fake, fake, kv, fake, fake, fake,
+                                             256, fake, B.STAR_BF16, None, None) == B.STAR_ERR_SHAPE
+    assert lib.star_attn_decode_step_noalloc(ctypes.byref(d), fake, fake, kv, None, fake, fake,
+                                             1, fake, B.STAR_BF16, None, None) == B.STAR_ERR_INVALID_ARG
+
+
 def test_binding_follows_the_header_abi_version():
     import re
     from long_context_attention_phase1_amd import binding
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "star_attn.h")).read()
     assert int(re.search(r"#define STAR_ATTN_ABI_VERSION (\d+)", hdr).group(1)) == binding.ABI_VERSION
+    m = re.search(r"#define STAR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert int(m.group(1)) << int(m.group(2)) == binding.STAR_NOALLOC_SCRATCH_BYTES
