@@ -104,9 +104,38 @@ def query_roofline(w, q_ms: float) -> dict:
     return r
 
 
-def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0):
+def host_info():
+    """The host the oracle runs on: cores available to this process, CPU model,
+    numpy's BLAS library and its thread count."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas_name = f"{dep.get('name')} {dep.get('version')}"
+    except Exception:  # older numpy: no dict form
+        blas_name = blas[0]["internal_api"] if blas else None
+    return {"cores_available": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "cpu_model": model, "blas": blas_name,
+            "blas_threads": blas[0]["num_threads"] if blas else None}
+
+
+def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0, gpu=None):
     """The oracle (as it stands) on a bounded sample of the same workload:
-    phase-1 context rows (the headline unit), then decode tokens."""
+    phase-1 context rows (the headline unit), then decode tokens.
+
+    ``gpu``: optional GPU results of the timed run (``o_ctx`` for sequence 0
+    and ``o_last``, the last decode step's output) that the sampled oracle
+    rows are also compared with, element by element (max-abs error)."""
     import numpy as np
 
     from long_context_attention_phase1_amd import synthetic as syn
@@ -121,12 +150,15 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0
     Ks = [wide(inputs["k_ctx"][0, :, g]) for g in range(w.n_kv_heads)]
     Vs = [wide(inputs["v_ctx"][0, :, g]) for g in range(w.n_kv_heads)]
     t0, c0 = time.perf_counter(), time.process_time()
-    done = 0
+    done, ref1 = 0, []
     for r in rows:
         r = int(r)
+        outs = []
         for g in range(w.n_kv_heads):
             q = wide(inputs["q_ctx"][0, r:r + 1, g * G:(g + 1) * G])
-            orc.phase1_rows_one_head(q, Ks[g], Vs[g], [r], w.block_len, w.anchor_len, sc)
+            outs.append(orc.phase1_rows_one_head(q, Ks[g], Vs[g], [r], w.block_len, w.anchor_len,
+                                                 sc))
+        ref1.append((r, outs))
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -150,12 +182,36 @@ def cpu_baseline(w, inputs, budget_s: float = 12.0, decode_budget_s: float = 6.0
             break
     dwall = time.perf_counter() - t1
     dcpu = time.process_time() - c1
-    return {"value": done / wall, "unit": "ctx tokens/s", "cores": max(1, round(cpu / wall)),
+    parity = None
+    if gpu is not None:
+        # the GPU's outputs of the timed run against the sampled oracle rows
+        e1 = 0.0
+        for r, outs in ref1:
+            o = gpu["o_ctx"][r]  # [Hq, d] float64
+            for g, ref in enumerate(outs):
+                e1 = max(e1, float(np.abs(o[g * G:(g + 1) * G] - ref[0]).max()))
+        row = w.n_query + w.n_decode - 1
+        e2, el = 0.0, 0.0
+        for g in range(w.n_kv_heads):
+            q = wide(inputs["q_tail"][0, row:row + 1, g * G:(g + 1) * G])
+            ro, rl = orc.phase2_rows_one_head(q, Kall[g], Vall[g], [w.ctx_len + row], sc)
+            e2 = max(e2, float(np.abs(gpu["o_last"][g * G:(g + 1) * G] - ro[0]).max()))
+            el = max(el, float(np.abs(gpu["lse_last"][g * G:(g + 1) * G] - rl[0]).max()))
+        parity = {"phase1_max_abs": e1, "phase1_rows": len(ref1),
+                  "last_decode_max_abs": e2, "last_decode_lse_max_abs": el,
+                  "sample": f"sequence 0: the {len(ref1)} timed phase-1 rows (all heads) and the "
+                            f"last decode token (all heads) of the timed run against the fp64 "
+                            f"oracle"}
+    info = host_info()
+    return {"value": done / wall, "unit": "ctx tokens/s", "cores": info["blas_threads"]
+            or info["cores_available"],
+            "achieved_parallelism": cpu / wall, "host": info, "parity": parity,
             "kind": "oracle",
             "sample": f"phase-1 fp64 oracle on {done} context rows drawn uniformly (seed 0) "
                       f"from sequence 0, all {w.n_q_heads} query heads, {wall:.1f} s wall",
             "decode": {"value": dwall * 1e6 / steps, "unit": "µs/token",
-                       "cores": max(1, round(dcpu / dwall)),
+                       "cores": info["blas_threads"] or info["cores_available"],
+                       "achieved_parallelism": dcpu / dwall,
                        "sample": f"dense fp64 oracle rows of the first {steps} decode tokens "
                                  f"of sequence 0, all {w.n_q_heads} query heads, "
                                  f"{dwall:.1f} s wall"}}
@@ -198,6 +254,45 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
+class _Rows:
+    """Rows of a device tensor, fetched one at a time as float64 host arrays."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, r):
+        return self.t[r].double().cpu().numpy()
+
+
+def decode_flushed(p, w, stream):
+    """One more decode loop, each step timed alone (HIP events on the launch
+    stream) right after a 512 MiB buffer is written, which evicts the KV
+    cache from the 256 MB last-level cache (MALL): the decode step as it runs
+    when its cache is not resident there."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=p.k_cache.device)
+    times, nbytes = [], []
+    for t in range(w.n_decode):
+        row = w.n_query + t
+        kv_len = w.ctx_len + row + 1
+        n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
+        flush.fill_(t & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        p.decode_call(kv_len, row, o_part, lse_part, o, lse)
+        e1.record(stream)
+        times.append((e0, e1))
+        nbytes.append(decode_bytes(w, kv_len))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in times])
+    gbs = float(np.sum(nbytes) / (np.sum(us) * 1e-6) / 1e9)
+    del flush
+    return {"us_per_step_median": float(np.median(us)), "us_per_step_mean": float(np.mean(us)),
+            "achieved_GBs": gbs, "frac_of_8TBs": gbs / PEAK_HBM_GBS,
+            "method": "each step timed alone after a 512 MiB device write (MALL flushed)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +311,10 @@ def main():
                          "block table; the context is written into the pages too")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="after the timed steps, time one more decode loop step by step with "
+                         "the 256 MB last-level cache (MALL) flushed before each step (a 512 MiB "
+                         "buffer written between steps, outside the timed events)")
     args = ap.parse_args()
     if args.paged and args.rope != "none":
         ap.error("--paged writes the context unrotated into the pages: use it without --rope")
@@ -374,8 +473,15 @@ def main():
             rq["frac_of_measured"] = rq["achieved"] / measured["hbm_read"]["value"]
         elif w.dtype == "bf16":
             rq["frac_of_measured"] = rq["achieved"] / measured["mfma_bf16"]["value"]
+    if args.flush_mall:
+        out["decode_mall_flushed"] = decode_flushed(p, w, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs)
+        row = w.n_query + w.n_decode - 1
+        _, _, _, o_last, lse_last = p.workspace(w.ctx_len + row + 1, 1)
+        gpu = {"o_ctx": _Rows(p.o_ctx[0]),
+               "o_last": o_last[0, 0].double().cpu().numpy(),
+               "lse_last": lse_last[0, 0].double().cpu().numpy()}
+        out["cpu_baseline"] = cpu_baseline(w, inputs, gpu=gpu)
     print(json.dumps(out), flush=True)
 
 

@@ -35,6 +35,36 @@ def test_cpu_baseline_reports_both_legs(name):
     assert "decode tokens" in d["sample"]
 
 
+def test_cpu_baseline_records_host_and_compares_gpu_outputs():
+    """The oracle leg states the host (cores available, CPU model, BLAS) and,
+    given a run's outputs, their max-abs error on the sampled rows: zero for
+    the oracle's own outputs, the planted offset for shifted ones."""
+    import numpy as np
+
+    from oracle import star_oracle as orc
+    w = syn.workload("tiny_f32")
+    x = {k: syn.to_f64(v, w.dtype) for k, v in syn.make_inputs(w).items()}
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    o1 = orc.phase1(x["q_ctx"], x["k_ctx"], x["v_ctx"], w.block_len, w.anchor_len, sc)[0]
+    ro, rl = orc.decode_loop(x["q_tail"], x["k_ctx"], x["v_ctx"], x["k_tail"], x["v_tail"],
+                             w.n_query, sc)
+    exact = {"o_ctx": o1, "o_last": ro[0, -1], "lse_last": rl[0, -1]}
+    inputs = syn.make_inputs(w)
+    cb = bench.cpu_baseline(w, inputs, budget_s=0.2, decode_budget_s=0.2, gpu=exact)
+    h = cb["host"]
+    assert h["cores_available"] >= 1 and h["cpu_count"] >= h["cores_available"]
+    assert h["blas"] and cb["cores"] >= 1 and cb["achieved_parallelism"] > 0
+    par = cb["parity"]
+    assert par["phase1_rows"] >= 1
+    assert par["phase1_max_abs"] < 1e-12 and par["last_decode_max_abs"] < 1e-12
+    assert par["last_decode_lse_max_abs"] < 1e-12
+    shifted = {"o_ctx": o1 + 1e-3, "o_last": ro[0, -1] - 2e-3, "lse_last": rl[0, -1] + 3e-3}
+    par = bench.cpu_baseline(w, inputs, budget_s=0.2, decode_budget_s=0.2, gpu=shifted)["parity"]
+    assert abs(par["phase1_max_abs"] - 1e-3) < 1e-9
+    assert abs(par["last_decode_max_abs"] - 2e-3) < 1e-9
+    assert abs(par["last_decode_lse_max_abs"] - 3e-3) < 1e-9
+
+
 def test_bench_config_of_a_command():
     from long_context_attention_phase1_amd.profiling import bench_config
     assert bench_config("python3 /root/repo/bench.py --steps 1 --no-cpu-baseline") == {
