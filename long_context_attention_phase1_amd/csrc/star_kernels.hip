@@ -533,6 +533,37 @@ __device__ __forceinline__ void qk_slice(const char* smem, const LaneOffsets<D, 
   }
 }
 
+// The first kKA K operands (k-steps) of a slice's QK, read from LDS ahead of
+// the chain into registers; qk_ahead runs the chain on them and reads the
+// rest as it goes. Holding four ahead takes the LDS latency off the start of
+// each half-stage (phase 1 at 128K 1.7% faster, bit-identical); all eight
+// ahead spill registers.
+constexpr int kKA = 4;
+
+template <int D, int NW, int ST, int KT>
+__device__ __forceinline__ void k_ahead(const char* smem, const LaneOffsets<D, NW>& lo,
+                                        u32x4 (&kop)[kKA]) {
+  using Gm = Geo<D, NW>;
+#pragma unroll
+  for (int ks = 0; ks < kKA; ++ks)
+    kop[ks] = lds16(smem + lo.kq[ks] + (Gm::K_AT + ST * Gm::KBYTES + KT * 32 * Gm::RB));
+}
+
+template <int D, int NW, int QT, int ST, int KT>
+__device__ __forceinline__ void qk_ahead(const char* smem, const LaneOffsets<D, NW>& lo,
+                                         const u32x4 (&kop)[kKA],
+                                         const u32x4 (&q)[QT][Geo<D, NW>::KS], f32x16 (&s)[QT]) {
+  using Gm = Geo<D, NW>;
+  static_assert(Gm::KS >= kKA, "head_dim too small for the operands read ahead");
+#pragma unroll
+  for (int ks = 0; ks < Gm::KS; ++ks) {
+    const u32x4 kv = ks < kKA ? kop[ks]
+                              : lds16(smem + lo.kq[ks] + (Gm::K_AT + ST * Gm::KBYTES + KT * 32 * Gm::RB));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) s[qt] = mfma_bf16(kv, q[qt][ks], ks == 0 ? f32x16{} : s[qt]);
+  }
+}
+
 // O^T += V^T P^T for one 32-key slice KT of stage ST.
 template <int D, int NW, int QT, int ST, int KT>
 __device__ __forceinline__ void pv_slice(const char* smem, const LaneOffsets<D, NW>& lo,
@@ -615,19 +646,24 @@ __device__ __forceinline__ void slice_exp2(const f32x16 (&s)[QT], const float (&
 
 // One 64-key stage of the software-pipelined interior loop: slice (t,0)
 // then slice (t,1); the first QK of the next stage is issued in the second
-// half, after the ring barrier and the DMA of tile t + 3.
+// half, after the ring barrier and the DMA of tile t + 3. `ka` holds the
+// first K operands of half A's QK (stage ST, slice 1), read at the end of the
+// previous stage; those of half B's QK (stage ST + 1, slice 0) are read right
+// after the barrier, and the stage ends by reading the next stage's half-A
+// operands (stage ST + 1 landed before the barrier).
 template <int D, int NW, int QT, int ST, bool NT>
 __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, NW>& lo,
                                                const u32x4 (&q)[QT][Geo<D, NW>::KS],
                                                f32x16 (&sc)[QT], float (&mx)[QT], float (&m)[QT],
                                                float (&l)[QT], f32x16 (&o)[QT][Geo<D, NW>::DT],
-                                               float c2, const char* Kt3, const char* Vt3, int w) {
+                                               u32x4 (&ka)[kKA], float c2, const char* Kt3,
+                                               const char* Vt3, int w) {
   using Gm = Geo<D, NW>;
   rescale_top<QT, Gm::DT>(mx, m, l, o, c2);
   {
     f32x16 sn[QT];
     u32x4 p[QT][2];
-    qk_slice<D, NW, QT, ST, 1>(smem, lo, q, sn);
+    qk_ahead<D, NW, QT, ST, 1>(smem, lo, ka, q, sn);
     slice_exp2<QT>(sc, m, l, p, c2);
     pv_slice<D, NW, QT, ST, 0>(smem, lo, p, o);
     slice_max3<QT>(sn, mx);
@@ -640,17 +676,22 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
   wait_vm_lgk0<Gm::PER>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");  // no LDS read moves above the wait
+  u32x4 kb[kKA];
+  k_ahead<D, NW, (ST + 1) & 3, 0>(smem, lo, kb);
   dma_stage_asm<D, NW, (ST + 3) & 3, NT>(smem, Kt3, Vt3, lo, w);
   {
     f32x16 sn[QT];
     u32x4 p[QT][2];
-    qk_slice<D, NW, QT, (ST + 1) & 3, 0>(smem, lo, q, sn);
+    qk_ahead<D, NW, QT, (ST + 1) & 3, 0>(smem, lo, kb, q, sn);
     slice_exp2<QT>(sc, m, l, p, c2);
     pv_slice<D, NW, QT, ST, 1>(smem, lo, p, o);
     slice_max3<QT>(sn, mx);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) sc[qt] = sn[qt];
   }
+  k_ahead<D, NW, (ST + 1) & 3, 1>(smem, lo, ka);
+  // keep these reads here, ahead of the next stage's rescale check
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wave -> columns: wave w owns QT column tiles of 32 (query row, head) pairs.
@@ -791,17 +832,19 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     float mx[QT];
     qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
     slice_max3<QT>(sc, mx);
+    u32x4 ka[kKA];
+    k_ahead<D, NW, 0, 1>(smem, lo, ka);
     for (int t = 0; t < n_int; t += 4) {
-      interior_stage<D, NW, QT, 0, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 0, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, ka, c2,
                                             Kc + tile_off(t + 3), Vc + tile_off(t + 3), w);
       if (t + 1 >= n_int) break;
-      interior_stage<D, NW, QT, 1, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 1, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, ka, c2,
                                             Kc + tile_off(t + 4), Vc + tile_off(t + 4), w);
       if (t + 2 >= n_int) break;
-      interior_stage<D, NW, QT, 2, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 2, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, ka, c2,
                                             Kc + tile_off(t + 5), Vc + tile_off(t + 5), w);
       if (t + 3 >= n_int) break;
-      interior_stage<D, NW, QT, 3, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, c2,
+      interior_stage<D, NW, QT, 3, KVNT>(smem, lo, qop, sc, mx, m, l, oacc, ka, c2,
                                             Kc + tile_off(t + 6), Vc + tile_off(t + 6), w);
     }
     wait_vmcnt<0>();

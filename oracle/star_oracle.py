@@ -313,6 +313,38 @@ def phase1_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
     return out
 
 
+def phase1_block_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
+                               rows: Sequence[int], block_len: int, anchor_len: int,
+                               scale: float) -> np.ndarray:
+    """Phase-1 outputs of sampled rows that all lie in one context block, for
+    the query heads of one kv head, with one product over the block's key set.
+
+    Same definition as ``phase1_rows_one_head`` (key set of
+    ``phase1_key_rows``): the rows of block ``i`` share the anchor ``[0, a)``
+    (for ``i >= 1``) and the block's rows up to the last sampled row; each
+    row masks the block keys after itself. ``q_rows``: ``[n, h, d]``;
+    ``K``, ``V``: ``[L', d]``. Returns ``[n, h, d]``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    i = int(rows[0]) // block_len
+    assert (rows // block_len == i).all(), "rows of one block"
+    lo, hi = i * block_len, int(rows.max()) + 1
+    anc = np.arange(anchor_len if i > 0 else 0, dtype=np.int64)
+    blk = np.arange(lo, hi, dtype=np.int64)
+    keys = np.concatenate([anc, blk])
+    Kk = np.asarray(K[keys], dtype=np.float64)
+    Vk = np.asarray(V[keys], dtype=np.float64)
+    q = np.asarray(q_rows, dtype=np.float64)
+    n, h, d = q.shape
+    S = scale * (q.reshape(n * h, d) @ Kk.T)                 # [n*h, |keys|]
+    # block key j (row lo + j) is visible to row r when lo + j <= r
+    visible = np.ones((n, len(keys)), dtype=bool)
+    visible[:, len(anc):] = blk[None, :] <= rows[:, None]
+    S = np.where(np.repeat(visible, h, axis=0), S, -np.inf)
+    out, _ = _softmax_rows(S, Vk)
+    return out.reshape(n, h, d)
+
+
 def phase2_rows_one_head(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
                          positions: Sequence[int], scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Dense phase-2 outputs and lse of sampled query rows for one kv head.

@@ -337,6 +337,31 @@ def pin_sampled_row_forms_match_sdpa(orc):
         _close(l, lref[0, :, g * 3:(g + 1) * 3], what=f"sampled phase2 lse g={g}")
 
 
+def pin_block_rows_form_matches_sdpa(orc):
+    """The block-batched sampled-row form against SDPA over [anchor ; block]
+    (block 0: plain causal attention), on every block, with a ragged last
+    block, a < b, GQA 3:1, rows in any order and repeated."""
+    B, L, Hq, Hkv, d = 1, 29, 6, 2, 8
+    q, k, v = _qkv(18, B, L, Hq, Hkv, d)
+    G = Hq // Hkv
+    sc = _scale(orc, d)
+    b, a = 8, 5
+    rng = np.random.default_rng(3)
+    for i in range(-(-L // b)):
+        lo, hi = i * b, min((i + 1) * b, L)
+        rows = list(rng.permutation(np.arange(lo, hi))) + [lo]
+        if i == 0:
+            ref = _sdpa(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], causal=True)
+        else:
+            cat = lambda x: np.concatenate([x[:, :a], x[:, lo:hi]], axis=1)
+            ref = _sdpa(cat(q), cat(k), cat(v), causal=True)[:, a:]
+        for g in range(Hkv):
+            o = orc.phase1_block_rows_one_head(q[0, rows, g * G:(g + 1) * G], k[0, :, g],
+                                               v[0, :, g], rows, b, a, sc)
+            _close(o, ref[0, [r - lo for r in rows], g * G:(g + 1) * G],
+                   what=f"block rows g={g} block {i}")
+
+
 # ------------------------------------------------------------------ rotary embedding
 
 def _angles(n_pos, d, theta=10000.0, offset=0):

@@ -156,3 +156,90 @@ def test_llama8b_32k_phase1_every_row():
     print(f"llama8b_32k: every row, every head; phase 1 max-abs {e:.3e}")
     assert e <= TOL_O
 
+
+
+def _tile_rows(w, s):
+    """One context row of every 64-row tile of every block (a row that moves
+    across the tile from tile to tile), and, for each, the query heads
+    checked: every head of the kv head's group when a workgroup covers all of
+    them (4 heads), else one head of each 4-head sub-group, rotating."""
+    rows = []
+    for i in range(w.n_blocks):
+        lo, hi = i * w.block_len, min((i + 1) * w.block_len, w.ctx_len)
+        for rt in range(-(-(hi - lo) // 64)):
+            r = min(lo + 64 * rt + (rt * 37 + i * 11 + s * 5) % 64, hi - 1)
+            rows.append((i, rt, r))
+    return rows
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama8b_128k_peaked", "llama70b_256k_b4"])
+def test_phase1_every_tile_and_bitwise_determinism(name):
+    """At full size, as the bench runs it: phase 1 twice and the whole tail
+    (query step and every decode step, fused) twice give identical bits; and
+    one row of every 64-row tile of every block, in every sequence, matches
+    the oracle for the heads of its workgroup (all of a kv head's query heads
+    at 4 per kv head; one head of every 4-head sub-group, rotating, at 8), so
+    every workgroup's output is checked at the full launch shape."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this environment")
+    w = syn.workload(name)
+    threads = min(16, os.cpu_count() or 1)
+    p = Pipeline(w, threads=threads, fill_nan=False)
+    p.write_context()
+    o1 = p.phase1().view(torch.int16).clone()
+    o2 = p.phase1().view(torch.int16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "phase 1 differs between two runs"
+    del o1
+    t1o, t1l = p.run_tail(fused=True)
+    t2o, t2l = p.run_tail(fused=True)
+    assert np.array_equal(t1o, t2o) and np.array_equal(t1l, t2l), "tail differs between runs"
+
+    x = p.inputs
+    sc = orc.resolve_scale(w.head_dim, 0.0)
+    G = w.group
+    picks = {s: _tile_rows(w, s) for s in range(w.batch)}
+    o_gpu = {s: to_host_f64(p.o_ctx[s, [r for _, _, r in picks[s]]]) for s in range(w.batch)}
+    del p
+
+    def errs(task):
+        s, g = task
+        K = syn.to_f64(x["k_ctx"][s, :, g], w.dtype)
+        V = syn.to_f64(x["v_ctx"][s, :, g], w.dtype)
+        e, n = 0.0, 0
+        idx = {r: j for j, (_, _, r) in enumerate(picks[s])}
+        for i in range(w.n_blocks):
+            blk = [(rt, r) for bi, rt, r in picks[s] if bi == i]
+            if G <= 4:  # one workgroup holds the kv head's heads: check them all
+                rows = [r for _, r in blk]
+                q = syn.to_f64(x["q_ctx"][s, rows, g * G:(g + 1) * G], w.dtype)
+                ref = orc.phase1_block_rows_one_head(q, K, V, rows, w.block_len, w.anchor_len,
+                                                     sc)
+                got = o_gpu[s][[idx[r] for r in rows]][:, g * G:(g + 1) * G]
+                e = max(e, float(np.abs(got - ref).max()))
+                n += ref.shape[0] * ref.shape[1]
+                continue
+            for hq in range(G // 4):
+                for hw in range(4):
+                    rows = [r for rt, r in blk if (rt + i) % 4 == hw]
+                    if not rows:
+                        continue
+                    h = g * G + hq * 4 + hw
+                    q = syn.to_f64(x["q_ctx"][s, rows, h:h + 1], w.dtype)
+                    ref = orc.phase1_block_rows_one_head(q, K, V, rows, w.block_len,
+                                                         w.anchor_len, sc)
+                    got = o_gpu[s][[idx[r] for r in rows]][:, h:h + 1]
+                    e = max(e, float(np.abs(got - ref).max()))
+                    n += len(rows)
+        return e, n
+
+    from threadpoolctl import threadpool_limits
+    tasks = [(s, g) for s in range(w.batch) for g in range(w.n_kv_heads)]
+    with threadpool_limits(1), ThreadPoolExecutor(min(len(tasks), threads)) as ex:
+        res = list(ex.map(errs, tasks))
+    e = max(r[0] for r in res)
+    n = sum(r[1] for r in res)
+    print(f"{name}: phase 1 and tail bitwise deterministic; {n} (row, head) outputs, one row per "
+          f"64-row tile of every block, max-abs {e:.3e}")
+    assert e <= TOL_O

@@ -96,6 +96,12 @@ MUTANTS = [
     ("decode_query_step_sees_all_tail",
      "[L + j for j in range(n_query)], scale)",
      "[L + n_query - 1 for j in range(n_query)], scale)"),
+    ("block_rows_see_own_future",
+     "visible[:, len(anc):] = blk[None, :] <= rows[:, None]",
+     "visible[:, len(anc):] = blk[None, :] <= rows[:, None] + 1"),
+    ("block_rows_anchor_on_block0",
+     "anc = np.arange(anchor_len if i > 0 else 0, dtype=np.int64)",
+     "anc = np.arange(anchor_len, dtype=np.int64)"),
     ("sampled_p1_no_anchor",
      "keys = phase1_key_rows(int(r), block_len, anchor_len)",
      "keys = phase1_key_rows(int(r), block_len, 0)[anchor_len * 0:] if r < block_len else np.arange(r // block_len * block_len, r + 1)"),
