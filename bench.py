@@ -265,32 +265,40 @@ class _Rows:
 
 
 def decode_flushed(p, w, stream):
-    """One more decode loop, each step timed alone (HIP events on the launch
-    stream) right after a 512 MiB buffer is written, which evicts the KV
-    cache from the 256 MB last-level cache (MALL): the decode step as it runs
-    when its cache is not resident there."""
+    """The decode loop with the KV cache evicted from the 256 MB last-level
+    cache (MALL) before every step: a 512 MiB device write before each step.
+    Timed as a loop of (flush, step) against a loop of the flushes alone, each
+    bracketed by HIP events on the launch stream with the queue never idle;
+    the difference over the steps is the step time on a cold MALL."""
     import numpy as np
     import torch
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=p.k_cache.device)
-    times, nbytes = [], []
-    for t in range(w.n_decode):
-        row = w.n_query + t
-        kv_len = w.ctx_len + row + 1
-        n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
-        flush.fill_(t & 255)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def loop(with_steps: bool) -> float:
+        e0, e1 = ev(), ev()
         e0.record(stream)
-        p.decode_call(kv_len, row, o_part, lse_part, o, lse)
+        for t in range(w.n_decode):
+            flush.fill_(t & 255)
+            if with_steps:
+                row = w.n_query + t
+                kv_len = w.ctx_len + row + 1
+                n_split, o_part, lse_part, o, lse = p.workspace(kv_len, 1)
+                p.decode_call(kv_len, row, o_part, lse_part, o, lse)
         e1.record(stream)
-        times.append((e0, e1))
-        nbytes.append(decode_bytes(w, kv_len))
-    torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) * 1e3 for a, b in times])
-    gbs = float(np.sum(nbytes) / (np.sum(us) * 1e-6) / 1e9)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    loop(True)  # warm-up
+    both = [loop(True) for _ in range(3)]
+    flushes = [loop(False) for _ in range(3)]
+    us = (float(np.median(both)) - float(np.median(flushes))) * 1e3 / w.n_decode
+    nbytes = sum(decode_bytes(w, w.ctx_len + w.n_query + t + 1) for t in range(w.n_decode))
+    gbs = nbytes / w.n_decode / (us * 1e-6) / 1e9
     del flush
-    return {"us_per_step_median": float(np.median(us)), "us_per_step_mean": float(np.mean(us)),
-            "achieved_GBs": gbs, "frac_of_8TBs": gbs / PEAK_HBM_GBS,
-            "method": "each step timed alone after a 512 MiB device write (MALL flushed)"}
+    return {"us_per_step": us, "achieved_GBs": gbs, "frac_of_8TBs": gbs / PEAK_HBM_GBS,
+            "method": "median of 3 loops of (512 MiB write, decode step) minus median of 3 "
+                      "loops of the writes alone, over the steps"}
 
 
 def main():

@@ -199,7 +199,8 @@ int star_attn_lse_merge(const star_attn_desc* desc, int64_t n_query, int32_t n_s
  *   3. merges them exactly as star_attn_lse_merge into o / lse_out.
  * When n_query * (n_q_heads / n_kv_heads) <= 32 and dtype is bf16, steps 1
  * and 2 are one kernel launch (the split that owns the new rows writes them
- * before reading them) and step 3 a second; otherwise three launches.
+ * before reading them) and step 3 a second; otherwise three launches (a
+ * query step of many tokens is one call too).
  * Argument checks as the three separate calls.
  */
 int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cache,

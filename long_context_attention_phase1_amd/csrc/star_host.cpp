@@ -143,8 +143,8 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
 static int decode_step_fits(const Dims& d, const Plan& p, int64_t kv_len, int64_t n_query) {
   if (p.n_split < 1 || !partial_fits(d, p, n_query) || !merge_fits(d, n_query))
     return STAR_ERR_SHAPE;
-  const bool fused = p.narrow && d.dtype == STAR_BF16;
-  if (!fused && !grid_fits(kv_write_grid(d, kv_len - n_query, n_query), 256)) return STAR_ERR_SHAPE;
+  if (!fused_append(d, p) && !grid_fits(kv_write_grid(d, kv_len - n_query, n_query), 256))
+    return STAR_ERR_SHAPE;
   return STAR_OK;
 }
 
@@ -253,10 +253,11 @@ int star_attn_decode_step(const star_attn_desc* desc, void* k_cache, void* v_cac
   const Plan p = make_plan(d, kv_len, n_query);
   st = decode_step_fits(d, p, kv_len, n_query);
   if (st) return st;
-  if (p.narrow && d.dtype == STAR_BF16)
+  if (fused_append(d, p))
     return launch_decode_step(d, p, k_cache, v_cache, kv_len, q, k_new, v_new, n_query, o_part,
                               lse_part, o, o_dtype, lse_out, stream);
-  // many query columns or fp32: the same three steps as separate launches
+  // fp32, or several workgroups per split: the same three steps as separate
+  // launches
   st = launch_kv_write(d, k_cache, v_cache, kv_len - n_query, k_new, v_new, n_query, stream);
   if (st) return st;
   st = launch_phase2_partial(d, p, k_cache, v_cache, kv_len, q, n_query, o_part, lse_part, stream);
@@ -285,7 +286,7 @@ int star_attn_decode_step_noalloc(const star_attn_desc* desc, void* k_cache, voi
   float* o_part = (float*)base;
   float* lse_part = (float*)((char*)base + noalloc_lse_offset(d, p, n_query));
   // the same launches as star_attn_decode_step, on the scratch partials
-  if (p.narrow && d.dtype == STAR_BF16)
+  if (fused_append(d, p))
     return launch_decode_step(d, p, k_cache, v_cache, kv_len, q, k_new, v_new, n_query, o_part,
                               lse_part, o, o_dtype, lse_out, stream);
   st = launch_kv_write(d, k_cache, v_cache, kv_len - n_query, k_new, v_new, n_query, stream);
@@ -363,7 +364,7 @@ int star_attn_decode_step_paged(const star_attn_desc* desc, void* k_pages, void*
   const Plan p = make_plan(d, kv_len, n_query);
   st = decode_step_fits(d, p, kv_len, n_query);
   if (st) return st;
-  if (p.narrow && d.dtype == STAR_BF16)
+  if (fused_append(d, p))
     return launch_decode_step(d, p, k_pages, v_pages, kv_len, q, k_new, v_new, n_query, o_part,
                               lse_part, o, o_dtype, lse_out, stream, block_table, max_pages);
   st = launch_kv_write(d, k_pages, v_pages, kv_len - n_query, k_new, v_new, n_query, stream,

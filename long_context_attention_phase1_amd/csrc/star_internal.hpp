@@ -319,6 +319,17 @@ STAR_HD static inline void narrow_map(int64_t bid, int32_t NG, int32_t n_split, 
   *sigma = n_split - 1 - (int32_t)(bid / NG);
 }
 
+// A decode step whose append runs inside the partial kernel: bf16 and at
+// most 32 query columns (the decode kernels, where the one workgroup that
+// holds the new rows is their only reader). Otherwise the append is a
+// kv_write launch of its own. (Appending inside the wide kernel of a query
+// step, whose splits also have one reader each, measured slower: that
+// split's workgroup starts after the first 256 and carries the append on the
+// launch's critical path.)
+static inline bool fused_append(const Dims& d, const Plan& p) {
+  return d.dtype == STAR_BF16 && p.narrow;
+}
+
 // ---- grid sizes of every launch, checked before a call enqueues anything
 //
 // HIP takes a grid as a 32-bit count of work-items: a launch whose

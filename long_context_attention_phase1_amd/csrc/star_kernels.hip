@@ -1846,7 +1846,72 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
   }
 }
 
+// The merge for many rows (a query step: n_query * Hq rows): one wave per
+// row, so that a launch holds thousands of light waves and streams the
+// partials at full bandwidth (the kernel above holds a row's splits in a
+// workgroup's registers at once: one memory round trip, the right shape for
+// the few rows of a decode step, but its registers cap how many workgroups a
+// CU holds). Lane l takes float4 column l % C4 and the splits congruent to
+// l / C4 modulo SPG = 64 / C4; the lanes of a column add their shares with
+// two (D = 128) or three (D = 64) exchanges.
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_rows_kernel(const MergeArgs a) {
+  constexpr int C4 = D / 4;     // float4 columns of a row
+  constexpr int SPG = 64 / C4;  // split groups in a wave
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int n = a.n_split;
+  const float* lp = a.lse_part + row * n;
+  const float4* op = (const float4*)(a.o_part + row * (int64_t)n * D);
+  // m = max_s lse_s, z = sum_s exp(lse_s - m) (every lane takes splits lane, lane + 64, ...)
+  float mx = -INFINITY;
+  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lp[i]);
+  mx = wave_max(mx);
+  const bool empty = mx == -INFINITY;
+  float z = 0.0f;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!empty) {
+    for (int i = lane; i < n; i += 64) z += expf(lp[i] - mx);
+    z = wave_sum(z);
+    const int c = lane % C4;
+    int i = lane / C4;
+#pragma unroll 4
+    for (; i < n; i += SPG) {
+      const float wgt = expf(lp[i] - mx);  // exp(-inf) = 0 for an empty split
+      const float4 v = op[(int64_t)i * C4 + c];
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
+    }
+#pragma unroll
+    for (int off = C4; off < 64; off <<= 1) {
+      acc.x += __shfl_xor(acc.x, off, 64);
+      acc.y += __shfl_xor(acc.y, off, 64);
+      acc.z += __shfl_xor(acc.z, off, 64);
+      acc.w += __shfl_xor(acc.w, off, 64);
+    }
+  }
+  if (lane < C4) {
+    const float inv = empty ? 0.0f : 1.0f / z;
+    const float v[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if (a.o_f32) {
+      ((float4*)a.o)[row * C4 + lane] = float4{v[0], v[1], v[2], v[3]};
+    } else {
+      uint2 b;
+      b.x = pack_bf16(v[0], v[1]);
+      b.y = pack_bf16(v[2], v[3]);
+      ((uint2*)a.o)[row * C4 + lane] = b;
+    }
+    if (lane == 0 && a.lse_out) a.lse_out[row] = empty ? -INFINITY : mx + logf(z);
+  }
+}
+
 int check_launch() { return hipGetLastError() == hipSuccess ? STAR_OK : STAR_ERR_HIP; }
+
+// Rows from which the merge takes one wave per row: four waves per CU.
+constexpr int64_t kMergeRowsPerWave = 1024;
 
 // kWideWaves (8 waves per wide-kernel workgroup): two per SIMD, 32 columns
 // each (four waves of 64 columns need more than the 512 registers of a lane
@@ -2224,8 +2289,15 @@ int launch_lse_merge(const Dims& d, int64_t n_query, int32_t n_split, const floa
   a.n_split = n_split;
   a.o_f32 = o_dtype == STAR_F32;
   if (!grid_fits(a.rows, 256)) return STAR_ERR_SHAPE;
-  const dim3 grid((unsigned)a.rows);
   hipStream_t st = (hipStream_t)stream;
+  if (a.rows >= kMergeRowsPerWave) {
+    // many rows: one wave per row, four rows per workgroup
+    const dim3 grid((unsigned)((a.rows + 3) / 4));
+    if (d.D == 128) hipLaunchKernelGGL((lse_merge_rows_kernel<128>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((lse_merge_rows_kernel<64>), grid, dim3(256), 0, st, a);
+    return check_launch();
+  }
+  const dim3 grid((unsigned)a.rows);
   if (d.D == 128) hipLaunchKernelGGL((lse_merge_kernel<128>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((lse_merge_kernel<64>), grid, dim3(256), 0, st, a);
   return check_launch();

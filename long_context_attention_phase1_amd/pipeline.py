@@ -127,9 +127,26 @@ class Pipeline:
         return o, lse
 
     def query_step(self):
+        """The query step as one call: append the n_query rows' K/V, the
+        partials and the merge (star_attn_decode_step[_paged] for n_query
+        rows)."""
+        w = self.w
+        kv_len = w.ctx_len + w.n_query
+        n_split, o_part, lse_part, o, lse = self.workspace(kv_len, w.n_query)
+        self.step_call(kv_len, self.q_query, self.k_query, self.v_query, w.n_query, o_part,
+                       lse_part, o, lse)
+        return o, lse
+
+    def query_step_separate(self):
+        """The query step as three calls: kv_write, partials, merge."""
         w = self.w
         self.kv_write2(w.ctx_len, self.k_query, self.v_query, w.n_query)
         return self.attend(w.ctx_len + w.n_query, self.q_query, w.n_query)
+
+    def step_call(self, kv_len, q, k, v, n_query, o_part, lse_part, o, lse):
+        """star_attn_decode_step for n_query rows ending at kv_len."""
+        sa.star_attn_decode_step(self.desc, self.k_cache, self.v_cache, kv_len, q, k, v, n_query,
+                                 o_part, lse_part, o, self.dtype, lse)
 
     def decode_step(self, t):
         """Decode step t (0-based): append tail row n_query + t, attend with it."""
@@ -148,9 +165,11 @@ class Pipeline:
         return o, lse
 
     def run_tail(self, fused=False):
-        """Query step then every decode step; returns host arrays [B, T, Hq, d], [B, T, Hq]."""
+        """Query step then every decode step; returns host arrays [B, T, Hq, d], [B, T, Hq].
+        fused: each step as one star_attn_decode_step call; else as the
+        separate kv_write, partial and merge calls."""
         w = self.w
-        o, lse = self.query_step()
+        o, lse = self.query_step() if fused else self.query_step_separate()
         outs, lses = [to_host_f64(o)], [lse.cpu().numpy().astype(np.float64)]
         for t in range(w.n_decode):
             o, lse = self.decode_step_fused(t) if fused else self.decode_step(t)
@@ -199,3 +218,7 @@ class PagedPipeline(Pipeline):
                                        self.q_tail_rows[row], self.k_tail_rows[row],
                                        self.v_tail_rows[row], 1, o_part, lse_part, o, self.dtype,
                                        lse)
+
+    def step_call(self, kv_len, q, k, v, n_query, o_part, lse_part, o, lse):
+        sa.star_attn_decode_step_paged(self.desc, self.k_pages, self.v_pages, self.table, kv_len,
+                                       q, k, v, n_query, o_part, lse_part, o, self.dtype, lse)

@@ -178,6 +178,7 @@ static void replay_wide2(const Dims& d, const Plan& p, int64_t kv_len, int64_t n
   const WideGeom gm = wide2_geom(d, p);
   const int QT = 8 / kWideWaves;
   Bits parts((int64_t)d.B * n_query * d.Hq * p.n_split);
+  CHECK(!fused_append(d, p));  // the wide kernel never appends
   const int64_t pos_off = kv_len - n_query;
   for (int64_t bid = 0; bid < gm.grid; ++bid) {
     int32_t gidx;

@@ -66,6 +66,10 @@ CASES = {
     # so the wide kernel keeps a kv head's work items on one XCD and reads
     # K/V with the default cache policy
     "kv_major_g8": W("kv_major", 2, 32, 4, 128, 640, 256, 256, 40, 1, "bf16", seed=21),
+    # query steps of 1,024 or more (query, head) rows: the merge takes one
+    # wave per row (d = 128 and 64, bf16 and fp32)
+    "many_rows_d64": W("many_rows_d64", 1, 16, 4, 64, 700, 256, 128, 70, 1, "bf16", seed=22),
+    "f32_many_rows": W("f32_many_rows", 1, 8, 2, 64, 200, 64, 32, 130, 1, "f32", seed=23),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
@@ -251,6 +255,47 @@ def test_phase2_is_deterministic():
     assert torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d,n_query,n_split", [(128, 80, 7), (64, 70, 40), (128, 20, 5)])
+def test_lse_merge_direct_against_oracle(d, n_query, n_split):
+    """star_attn_lse_merge on crafted partials: random vectors and lse values,
+    empty splits (lse = -inf) scattered, one row with no visible key at all.
+    The first two shapes have 1,024 or more rows (one wave per row), the last
+    fewer (one workgroup per row)."""
+    _need_gpu()
+    Hq = 16
+    desc = sa.make_desc(1, Hq, 4, d, 64, 64, 64, n_query, sa.STAR_F32)
+    rng = np.random.default_rng(d + n_query)
+    rows = n_query * Hq
+    o_part = rng.standard_normal((rows, n_split, d)).astype(np.float32)
+    lse = (rng.standard_normal((rows, n_split)) * 3.0).astype(np.float32)
+    lse[rng.random((rows, n_split)) < 0.2] = -np.inf
+    o_part[np.isinf(lse)] = 0.0  # an empty split's vector is zero, as the kernels write it
+    lse[5] = -np.inf
+    o_part[5] = 0.0
+    dev = lambda x: torch.from_numpy(x).cuda()
+    op = dev(o_part).view(1, n_query, Hq, n_split, d)
+    lp = dev(lse).view(1, n_query, Hq, n_split)
+    o = torch.empty(1, n_query, Hq, d, dtype=torch.float32, device="cuda")
+    ob = torch.empty(1, n_query, Hq, d, dtype=torch.bfloat16, device="cuda")
+    l_out = torch.empty(1, n_query, Hq, dtype=torch.float32, device="cuda")
+    sa.star_attn_lse_merge(desc, n_query, n_split, op, lp, o, sa.STAR_F32, l_out)
+    sa.star_attn_lse_merge(desc, n_query, n_split, op, lp, ob, sa.STAR_BF16, None)
+    torch.cuda.synchronize()
+    got = o.cpu().numpy().reshape(rows, d).astype(np.float64)
+    gotb = ob.float().cpu().numpy().reshape(rows, d).astype(np.float64)
+    gl = l_out.cpu().numpy().reshape(rows).astype(np.float64)
+    eo = el = eb = 0.0
+    for r in range(rows):
+        ro, rl = orc.lse_merge(o_part[r].astype(np.float64), lse[r])
+        eo = max(eo, float(np.abs(got[r] - ro).max()))
+        eb = max(eb, float(np.abs(gotb[r] - ro).max()))
+        if np.isinf(rl):
+            assert gl[r] == -np.inf and not got[r].any()
+        else:
+            el = max(el, abs(gl[r] - rl))
+    assert eo <= 1e-5 and el <= 1e-5 and eb <= 2e-2, (eo, el, eb)
+
+
 def test_binding_rejects_wrong_buffers():
     _need_gpu()
     w = CASES["g8_narrow"]
@@ -270,7 +315,9 @@ def test_binding_rejects_wrong_buffers():
                                   "f32_b1"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
-    decode loop and against the three separate calls, every step."""
+    decode loop and against the three separate calls, every step: the query
+    step (n_query rows in one call: the append fused into the wide kernel
+    when one workgroup reads each split) and every decode step."""
     p0, _, tail_o, tail_l = _pipeline(runs, name)
     w = p0.w
     p = Pipeline(w, inputs=p0.inputs, threads=4)
@@ -281,9 +328,9 @@ def test_fused_decode_step(runs, name):
     sc = orc.resolve_scale(w.head_dim, 0.0)
     ref_o, ref_l = orc.decode_loop(x["q_tail"], x["k_ctx"], x["v_ctx"], x["k_tail"],
                                    x["v_tail"], w.n_query, sc)
-    d = slice(w.n_query, None)
+    d = slice(0, None)
     eo, el = _err(fo[:, d], ref_o[:, d]), _err(fl[:, d], ref_l[:, d])
-    print(f"{name}: fused decode max-abs error o {eo:.3e}, lse {el:.3e}")
+    print(f"{name}: fused query and decode steps max-abs error o {eo:.3e}, lse {el:.3e}")
     assert eo <= TOL[w.dtype] and el <= TOL_LSE[w.dtype]
     # same partial arithmetic as the separate calls: outputs agree to the
     # output rounding (bf16: one ulp of |o| < 8 is 2^-5 at most)
