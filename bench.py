@@ -266,20 +266,22 @@ class _Rows:
 
 def decode_flushed(p, w, stream):
     """The decode loop with the KV cache evicted from the 256 MB last-level
-    cache (MALL) before every step: a 512 MiB device write before each step.
-    Timed as a loop of (flush, step) against a loop of the flushes alone, each
-    bracketed by HIP events on the launch stream with the queue never idle;
-    the difference over the steps is the step time on a cold MALL."""
+    cache (MALL) before every step: a 512 MiB device read (a sum) before each
+    step. A read leaves no dirty lines behind, so the step pays no write-back
+    of the flush buffer. Timed as a loop of (flush, step) against a loop of
+    the flushes alone, each bracketed by HIP events on the launch stream with
+    the queue never idle; the difference over the steps is the step time on a
+    cold MALL."""
     import numpy as np
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=p.k_cache.device)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=p.k_cache.device)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def loop(with_steps: bool) -> float:
         e0, e1 = ev(), ev()
         e0.record(stream)
         for t in range(w.n_decode):
-            flush.fill_(t & 255)
+            flush.sum()
             if with_steps:
                 row = w.n_query + t
                 kv_len = w.ctx_len + row + 1
@@ -297,16 +299,78 @@ def decode_flushed(p, w, stream):
     gbs = nbytes / w.n_decode / (us * 1e-6) / 1e9
     del flush
     return {"us_per_step": us, "achieved_GBs": gbs, "frac_of_8TBs": gbs / PEAK_HBM_GBS,
-            "method": "median of 3 loops of (512 MiB write, decode step) minus median of 3 "
-                      "loops of the writes alone, over the steps"}
+            "method": "median of 3 loops of (512 MiB read, decode step) minus median of 3 "
+                      "loops of the reads alone, over the steps"}
+
+
+def gfx_clock_during(fn, n: int, device: int = 0, period_s: float = 0.002):
+    """The graphics (shader) clock in MHz, sampled through amdsmi from a host
+    thread while n launches of fn run back to back on the GPU (enqueued before
+    sampling starts, so the sampler never delays a launch). A record with an
+    "error" field when amdsmi or the device's handle is not available."""
+    import threading
+
+    import numpy as np
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # no amdsmi, or no access to the driver's interface
+        return {"error": f"amdsmi unavailable: {e}"}
+    try:
+        hs = amdsmi.amdsmi_get_processor_handles()
+        prop = torch.cuda.get_device_properties(device)
+        bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}"
+        match = [h for h in hs if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(bdf)]
+        h = match[0] if match else (hs[0] if len(hs) == 1 else None)
+        if h is None:
+            return {"error": f"no amdsmi handle for the GPU at {bdf}"}
+        gfx = amdsmi.AmdSmiClkType.GFX
+        samples = []
+        stop = threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    samples.append(float(amdsmi.amdsmi_get_clock_info(h, gfx)["clk"]))
+                except Exception:
+                    pass
+                stop.wait(period_s)
+
+        torch.cuda.synchronize()
+        for _ in range(n):
+            fn()
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return {"error": "amdsmi returned no clock samples"}
+        return {"median_mhz": float(np.median(samples)), "min_mhz": min(samples),
+                "max_mhz": max(samples), "samples": len(samples),
+                "method": f"amdsmi GFX clock every {period_s * 1e3:g} ms over {n} phase-1 "
+                          f"launches after the timed steps"}
+    except Exception as e:
+        return {"error": f"amdsmi clock query failed: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", "--reps", dest="steps", type=int, default=10,
+                    help="timed steps (one step: context write, phase 1, query step, "
+                         "decode loop)")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama8b_128k_peaked")
+    ap.add_argument("--workload", "--config", dest="workload", default="llama8b_128k_peaked",
+                    help="a workload of synthetic.WORKLOADS or synthetic.SWEEPS")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the workload's, 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the peak probes (libstarpeaks.so) run after the timed steps")
@@ -320,9 +384,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--flush-mall", action="store_true",
-                    help="after the timed steps, time one more decode loop step by step with "
-                         "the 256 MB last-level cache (MALL) flushed before each step (a 512 MiB "
-                         "buffer written between steps, outside the timed events)")
+                    help="after the timed steps, time the decode loop with the 256 MB "
+                         "last-level cache (MALL) flushed before each step (a 512 MiB buffer "
+                         "read between steps; the reads alone are timed and taken off)")
     args = ap.parse_args()
     if args.paged and args.rope != "none":
         ap.error("--paged writes the context unrotated into the pages: use it without --rope")
@@ -339,6 +403,8 @@ def main():
     from long_context_attention_phase1_amd.pipeline import PagedPipeline, Pipeline
 
     w = syn.workload(args.workload)
+    if args.seed is not None:
+        w = w.replace(seed=args.seed)
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
@@ -427,6 +493,8 @@ def main():
               f"lse_merge_kernel<{w.head_dim}>")
     bcfg = {"workload": args.workload, "paged": bool(args.paged), "rope": args.rope}
     t1, t2 = load_traffic(bcfg, kname1), load_traffic(bcfg, *kname2)
+    # the shader clock phase 1 runs at (outside the timed region)
+    clock = gfx_clock_during(p.phase1 if rope is None else (lambda: p.phase1_rope(rope)), 3)
     # measured peaks (after the timed region): the rates each roofline is also
     # read against, beside the published peaks
     measured = None
@@ -450,7 +518,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ctx_len": w.ctx_len,
                    "block_len": w.block_len, "anchor_len": w.anchor_len,
-                   "n_query": w.n_query, "n_decode": w.n_decode,
+                   "n_query": w.n_query, "n_decode": w.n_decode, "seed": w.seed,
                    "peaked_k_rows": w.peak_frac, "peak_factor": w.peak_factor,
                    "phase2_cache": "paged" if args.paged else "contiguous",
                    "rope": args.rope},
@@ -470,6 +538,7 @@ def main():
                                            "new K/V row written, one fp32 reply per host "
                                            "written and re-read, output row written"},
         "roofline_query": query_roofline(w, q_ms),
+        "gfx_clock_phase1": clock,
     }
     if measured is not None:
         out["measured_peaks"] = measured

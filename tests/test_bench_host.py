@@ -99,3 +99,21 @@ def test_query_step_work_and_bound():
         t_bound = max(flop / 2.5e15, nbytes / 8e12)
         assert abs(r["frac"] - t_bound / 1e-3) < 1e-12
         assert r["frac_other_bound"] <= r["frac"]
+
+
+def test_clock_sampler_reports_why_it_has_no_clock_without_a_gpu():
+    # on a host without the GPU driver the record names the reason instead of
+    # failing the bench line
+    rec = bench.gfx_clock_during(lambda: None, 1)
+    assert set(rec) == {"error"} and rec["error"]
+
+
+def test_flag_spellings_of_the_bench_record(monkeypatch, capsys):
+    # --config, --reps and --seed are spellings the bench record documents;
+    # --gpus above 1 stops before anything touches a GPU
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2", "--config", "llama8b_32k",
+                                     "--reps", "3", "--seed", "7"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
