@@ -182,11 +182,12 @@ SIMDS, CUS, XCDS = 1024, 256, 8
 
 
 def counters(out_txt: str, dirs, command: str, kernels=None) -> None:
-    """Per-kernel counter totals over the given --pmc runs (one dispatch of
-    each kernel of interest per run). A counter taken in several runs (the
-    GRBM_GUI_ACTIVE reference) is averaged over them."""
-    vals = defaultdict(lambda: defaultdict(list))  # kernel -> counter -> per-run totals
-    durs = defaultdict(list)                        # kernel -> per-run dispatch duration (s)
+    """Per-kernel counters per dispatch over the given --pmc runs: each run's
+    total for a kernel over the number of its dispatches in that run. A
+    counter taken in several runs (the GRBM_GUI_ACTIVE reference) is averaged
+    over them."""
+    vals = defaultdict(lambda: defaultdict(list))  # kernel -> counter -> per-run means
+    durs = defaultdict(list)                        # kernel -> dispatch durations (s)
     for d in dirs:
         run = defaultdict(lambda: defaultdict(float))
         spans = {}
@@ -196,13 +197,16 @@ def counters(out_txt: str, dirs, command: str, kernels=None) -> None:
                 continue
             run[k][r["Counter_Name"]] += float(r["Counter_Value"])
             spans[(k, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-        for k, c in run.items():
-            for name, v in c.items():
-                vals[k][name].append(v)
+        n_disp = defaultdict(int)
         for (k, _), t in spans.items():
             durs[k].append(t)
-    lines = ["# rocprofv3 --pmc counters per kernel (summed over the XCDs and shader engines;",
-             "# GRBM_GUI_ACTIVE averaged over the runs that took it)",
+            n_disp[k] += 1
+        for k, c in run.items():
+            for name, v in c.items():
+                vals[k][name].append(v / n_disp[k])
+    lines = ["# rocprofv3 --pmc counters per kernel and dispatch (summed over the XCDs and shader",
+             "# engines, averaged over the kernel's dispatches; GRBM_GUI_ACTIVE averaged over the",
+             "# runs that took it)",
              f"# command: {command}",
              f"# native source (csrc/) sha256[:16]: {source_sha()}"]
     for k, cl in vals.items():

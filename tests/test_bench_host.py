@@ -117,3 +117,27 @@ def test_flag_spellings_of_the_bench_record(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_counter_summary_is_per_dispatch(tmp_path):
+    # two dispatches of one kernel in a run: the summary reports one
+    # dispatch's counters, so the engine clock (active cycles over the
+    # dispatch duration) does not grow with the number of launches
+    from long_context_attention_phase1_amd import profiling
+    k = "void star::(anonymous namespace)::attn_wide_kernel<128, 8, 1, true, false, 0, false>(WideArgs)"
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+    for disp in (1, 2):
+        t0 = disp * 10**9
+        # 8 XCDs x 2.0e6 active cycles over 1 ms: a 2.0 GHz clock
+        rows.append(f'{disp},"{k}",GRBM_GUI_ACTIVE,{8 * 2.0e6},{t0},{t0 + 10**6}')
+        rows.append(f'{disp},"{k}",SQ_INSTS_MFMA,1000,{t0},{t0 + 10**6}')
+        rows.append(f'{disp},"{k}",SQ_INSTS_VALU,5800,{t0},{t0 + 10**6}')
+    d = tmp_path / "run"
+    d.mkdir()
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    out = tmp_path / "c.txt"
+    profiling.counters(str(out), [str(d)], "cmd")
+    text = out.read_text()
+    assert "SQ_INSTS_MFMA                    1.000000e+03" in text
+    assert "effective engine clock (active / duration) 2.000 GHz" in text
+    assert "non-MFMA VALU instructions per MFMA        4.80" in text
