@@ -303,11 +303,14 @@ def decode_flushed(p, w, stream):
                       "loops of the reads alone, over the steps"}
 
 
-def gfx_clock_during(fn, n: int, device: int = 0, period_s: float = 0.002):
-    """The graphics (shader) clock in MHz, sampled through amdsmi from a host
-    thread while n launches of fn run back to back on the GPU (enqueued before
-    sampling starts, so the sampler never delays a launch). A record with an
+def gfx_clock_during(fn, launch_ms: float, device: int = 0, busy_s: float = 1.5,
+                     period_s: float = 0.05):
+    """The graphics clock of each XCD while fn (one launch of launch_ms) runs
+    back to back for about busy_s, read from the SMU's metrics table through
+    amdsmi by a host thread. The table refreshes about once a second, so only
+    the samples of the second half of the busy window count. A record with an
     "error" field when amdsmi or the device's handle is not available."""
+    import math
     import threading
 
     import numpy as np
@@ -325,32 +328,47 @@ def gfx_clock_during(fn, n: int, device: int = 0, period_s: float = 0.002):
         h = match[0] if match else (hs[0] if len(hs) == 1 else None)
         if h is None:
             return {"error": f"no amdsmi handle for the GPU at {bdf}"}
-        gfx = amdsmi.AmdSmiClkType.GFX
-        samples = []
+        samples = []  # (seconds since the launches were enqueued, per-XCD MHz, socket W)
         stop = threading.Event()
 
-        def sample():
+        def sample(t0):
             while not stop.is_set():
                 try:
-                    samples.append(float(amdsmi.amdsmi_get_clock_info(h, gfx)["clk"]))
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    clks = [float(c) for c in m.get("current_gfxclks", []) if isinstance(c, int)]
+                    if not clks and isinstance(m.get("current_gfxclk"), int):
+                        clks = [float(m["current_gfxclk"])]
+                    pw = m.get("current_socket_power")
+                    samples.append((time.perf_counter() - t0, clks,
+                                    float(pw) if isinstance(pw, int) else None))
                 except Exception:
                     pass
                 stop.wait(period_s)
 
+        n = max(3, min(4000, math.ceil(busy_s * 1e3 / max(launch_ms, 1e-3))))
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for _ in range(n):
             fn()
-        th = threading.Thread(target=sample, daemon=True)
+        th = threading.Thread(target=sample, args=(t0,), daemon=True)
         th.start()
         torch.cuda.synchronize()
+        busy = time.perf_counter() - t0
         stop.set()
         th.join()
-        if not samples:
-            return {"error": "amdsmi returned no clock samples"}
-        return {"median_mhz": float(np.median(samples)), "min_mhz": min(samples),
-                "max_mhz": max(samples), "samples": len(samples),
-                "method": f"amdsmi GFX clock every {period_s * 1e3:g} ms over {n} phase-1 "
-                          f"launches after the timed steps"}
+        late = [(c, w) for t, c, w in samples if busy / 2 <= t <= busy and c]
+        if not late:
+            return {"error": f"no clock sample in the second half of a {busy:.2f} s busy window"}
+        per_xcd = np.median(np.array([c for c, _ in late]), axis=0)
+        power = [w for _, w in late if w is not None]
+        return {"xcd_mhz": [round(float(x)) for x in per_xcd],
+                "mean_mhz": float(per_xcd.mean()), "min_mhz": float(per_xcd.min()),
+                "max_mhz": float(per_xcd.max()),
+                "socket_power_w": float(np.median(power)) if power else None,
+                "samples": len(late),
+                "method": f"amdsmi metrics (current_gfxclks per XCD), {len(late)} samples in the "
+                          f"second half of {n} back-to-back phase-1 launches ({busy:.2f} s), after "
+                          f"the timed steps"}
     except Exception as e:
         return {"error": f"amdsmi clock query failed: {e}"}
     finally:
@@ -494,7 +512,7 @@ def main():
     bcfg = {"workload": args.workload, "paged": bool(args.paged), "rope": args.rope}
     t1, t2 = load_traffic(bcfg, kname1), load_traffic(bcfg, *kname2)
     # the shader clock phase 1 runs at (outside the timed region)
-    clock = gfx_clock_during(p.phase1 if rope is None else (lambda: p.phase1_rope(rope)), 3)
+    clock = gfx_clock_during(p.phase1 if rope is None else (lambda: p.phase1_rope(rope)), p1_ms)
     # measured peaks (after the timed region): the rates each roofline is also
     # read against, beside the published peaks
     measured = None

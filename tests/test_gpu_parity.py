@@ -312,12 +312,14 @@ def test_binding_rejects_wrong_buffers():
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g8_narrow", "peaked", "ragged_empty_split",
                                   "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks",
                                   "balanced_bnd", "balanced_b2_g8_d64", "b1_a1", "ctx1",
-                                  "f32_b1"])
+                                  "f32_b1", "b1_wide_tail", "g2_d64_wide_tail", "long_tail_wide",
+                                  "kv_major_g8", "many_rows_d64"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
     decode loop and against the three separate calls, every step: the query
-    step (n_query rows in one call: the append fused into the wide kernel
-    when one workgroup reads each split) and every decode step."""
+    step (n_query rows in one call) and every decode step. The wide shapes
+    (more than 32 columns) cover one and several query tiles and head
+    sub-groups."""
     p0, _, tail_o, tail_l = _pipeline(runs, name)
     w = p0.w
     p = Pipeline(w, inputs=p0.inputs, threads=4)
