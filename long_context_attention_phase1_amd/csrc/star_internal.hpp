@@ -217,6 +217,12 @@ STAR_HD static inline void wide_map(int64_t bid, bool phase1, int32_t NG, int32_
   }
 }
 
+// Phase 2 on the wide kernel: one query tile with at most half its rows live
+// (the waves holding the other half only load tiles and meet barriers).
+static inline bool wide2_short(const WideGeom& g, int64_t n_query) {
+  return g.NRT == 1 && 2 * n_query <= g.BM;
+}
+
 // Phase 1: work item -> (block i, row tile rt). Anchored blocks go first, one
 // after another, each by descending row tile (the heaviest first), then
 // block 0: the workgroups an XCD runs at once are neighbouring row tiles of
@@ -265,7 +271,16 @@ STAR_HD static inline TileRuns tile_runs(int64_t hiA, int64_t loB, int64_t hiB, 
 // Wide kernel, wave w of a workgroup -> its first query row (relative to the
 // workgroup's first row) and the head hw (of the HW heads of the workgroup)
 // of its 32*QT columns: WPR = 2/QT waves share one 64-row sub-tile of one head.
-STAR_HD static inline void wide_wave(int w, int QT, int HW, int* hw, int64_t* row_off) {
+// Short query tile (phase 2, QT = 1, at most half the rows live): wave w takes
+// rows 32*(w / HW) of head w % HW, so waves 4..7, which share SIMDs with
+// waves 0..3, hold the idle rows.
+STAR_HD static inline void wide_wave(int w, int QT, int HW, bool short_tile, int* hw,
+                                     int64_t* row_off) {
+  if (short_tile) {
+    *hw = w % HW;
+    *row_off = (int64_t)(w / HW) * 32;
+    return;
+  }
   const int WPR = 2 / QT;
   const int wsub = w % WPR, wh = w / WPR;  // 32*QT-row piece, (head, 64-row sub-tile)
   *hw = wh % HW;

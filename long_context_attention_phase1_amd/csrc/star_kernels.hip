@@ -644,6 +644,18 @@ __device__ __forceinline__ void slice_exp2(const f32x16 (&s)[QT], const float (&
   }
 }
 
+// A stage of the interior loop for a wave with no live query row: the same
+// wait, barrier and tile load as interior_stage, no arithmetic.
+template <int D, int NW, int ST, bool NT>
+__device__ __forceinline__ void idle_stage(char* smem, const LaneOffsets<D, NW>& lo,
+                                           const char* Kt3, const char* Vt3, int w) {
+  using Gm = Geo<D, NW>;
+  wait_vm_lgk0<Gm::PER>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  dma_stage_asm<D, NW, (ST + 3) & 3, NT>(smem, Kt3, Vt3, lo, w);
+}
+
 // One 64-key stage of the software-pipelined interior loop: slice (t,0)
 // then slice (t,1); the first QK of the next stage is issued in the second
 // half, after the ring barrier and the DMA of tile t + 3. `ka` holds the
@@ -700,15 +712,19 @@ __device__ __forceinline__ void interior_stage(char* smem, const LaneOffsets<D, 
 // takes it when each split's keys are read by one workgroup; when several
 // workgroups read them (query-head sub-groups, query tiles), and in phase 1,
 // the default policy lets L2 serve the re-reads.
-template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE, bool KVNT>
-__global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
+// SHORT (phase 2): a query tile with at most half its rows live; the waves
+// without live rows load their share of every tile and meet every barrier,
+// but skip the arithmetic (see wide_wave).
+template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE, bool KVNT, bool SHORT>
+__device__ __forceinline__ void wide_body(const WideArgs& a, char* smem) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
   static_assert(!(PHASE1 && KVNT), "phase 1 reuses its tiles through L2");
   static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
+  static_assert(!(PHASE1 && SHORT), "short query tiles are a phase-2 case");
+  static_assert(!SHORT || QT == 1, "short tiles: one 32-column tile per wave");
   using Gm = Geo<D, NW>;
   constexpr int KS = Gm::KS, DT = Gm::DT;
   static_assert(NW * QT == 8, "workgroup covers 256 columns");
-  __shared__ __attribute__((aligned(1024))) char smem[Gm::RING];
   // the wave index is uniform: keep it (and what derives from it) scalar
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
@@ -721,7 +737,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
   const int kvh = t2 % a.Hkv, s = t2 / a.Hkv;
   int hw;
   int64_t wrow_off;  // this wave's first query row, from the workgroup's
-  wide_wave(w, QT, a.HW, &hw, &wrow_off);
+  wide_wave(w, QT, a.HW, SHORT, &hw, &wrow_off);
   const int head = kvh * a.G + hq * a.HW + hw;
 
   int64_t row0, row_end, hiA = 0, loB, hiB, pos_off;
@@ -748,6 +764,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     pos_off = a.kv_len - a.q_tokens;
   }
   const int64_t wrow0 = row0 + wrow_off;  // this wave's first query row
+  const bool idle = SHORT && wrow0 >= row_end;  // no live row: loads and barriers only
   const int64_t head_row0 = ((int64_t)s * a.Hkv + kvh) * a.rows;
   const uint16_t* K = PAGED ? a.k : a.k + head_row0 * D;
   const uint16_t* V = PAGED ? a.v : a.v + head_row0 * D;
@@ -828,6 +845,21 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
     wait_vmcnt<2 * Gm::PER>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS read moves above the wait
+    if (idle) {
+      // the same waits, barriers and tile loads as interior_stage
+      for (int t = 0; t < n_int; t += 4) {
+        idle_stage<D, NW, 0, KVNT>(smem, lo, Kc + tile_off(t + 3), Vc + tile_off(t + 3), w);
+        if (t + 1 >= n_int) break;
+        idle_stage<D, NW, 1, KVNT>(smem, lo, Kc + tile_off(t + 4), Vc + tile_off(t + 4), w);
+        if (t + 2 >= n_int) break;
+        idle_stage<D, NW, 2, KVNT>(smem, lo, Kc + tile_off(t + 5), Vc + tile_off(t + 5), w);
+        if (t + 3 >= n_int) break;
+        idle_stage<D, NW, 3, KVNT>(smem, lo, Kc + tile_off(t + 6), Vc + tile_off(t + 6), w);
+      }
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      return;
+    }
     f32x16 sc[QT];
     float mx[QT];
     qk_slice<D, NW, QT, 0, 0>(smem, lo, qop, sc);
@@ -874,6 +906,7 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
       et.load(K + tile_at(kbase / 64), V + tile_at(kbase / 64), kbase, klo, khi, tid);
       et.store(smem, tid);
       block_sync_lds();
+      if (!idle)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 sc[QT];
@@ -949,6 +982,20 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
       if (g == 0) a.lse_part[base] = any ? m[qt] * a.scale + logf(lt) : -INFINITY;
     }
   }
+}
+
+template <int D, int NW, int QT, bool PHASE1, bool PAGED, int ROPE, bool KVNT>
+__global__ __launch_bounds__(64 * NW) void attn_wide_kernel(const WideArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Geo<D, NW>::RING];
+  wide_body<D, NW, QT, PHASE1, PAGED, ROPE, KVNT, false>(a, smem);
+}
+
+// Phase 2 with a short query tile (wide2_short): the waves that hold no live
+// row leave the matrix cores to their SIMD partners.
+template <int D, int NW, bool PAGED, bool KVNT>
+__global__ __launch_bounds__(64 * NW) void attn_wide_short_kernel(const WideArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Geo<D, NW>::RING];
+  wide_body<D, NW, 1, false, PAGED, kRopeNone, KVNT, true>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -2191,6 +2238,21 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
   const dim3 grid((unsigned)gm.grid);
   // one reader per split: a non-temporal stream; several: L2 serves the rest
   const bool kv_nt = a.HQ * a.NRT == 1;
+  if (wide2_short(gm, n_query)) {
+    if (d.D == 128 && kv_nt)
+      hipLaunchKernelGGL((attn_wide_short_kernel<128, kWideWaves, PAGED, true>), grid,
+                         dim3(64 * kWideWaves), 0, st, a);
+    else if (d.D == 128)
+      hipLaunchKernelGGL((attn_wide_short_kernel<128, kWideWaves, PAGED, false>), grid,
+                         dim3(64 * kWideWaves), 0, st, a);
+    else if (kv_nt)
+      hipLaunchKernelGGL((attn_wide_short_kernel<64, kWideWaves, PAGED, true>), grid,
+                         dim3(64 * kWideWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_wide_short_kernel<64, kWideWaves, PAGED, false>), grid,
+                         dim3(64 * kWideWaves), 0, st, a);
+    return check_launch();
+  }
   if (d.D == 128 && kv_nt)
     hipLaunchKernelGGL((attn_wide_kernel<128, kWideWaves, 8 / kWideWaves, false, PAGED, kRopeNone, true>),
                        grid, dim3(64 * kWideWaves), 0, st, a);

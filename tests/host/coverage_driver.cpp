@@ -147,7 +147,7 @@ static void replay_phase1(const Dims& d) {
     for (int w = 0; w < kWideWaves; ++w) {
       int hw;
       int64_t off;
-      wide_wave(w, QT, d.HW, &hw, &off);
+      wide_wave(w, QT, d.HW, false, &hw, &off);
       const int head = kvh * d.G + hq * d.HW + hw;
       CHECK(head >= 0 && head < d.Hq);
       for (int qt = 0; qt < QT; ++qt)
@@ -180,6 +180,8 @@ static void replay_wide2(const Dims& d, const Plan& p, int64_t kv_len, int64_t n
   Bits parts((int64_t)d.B * n_query * d.Hq * p.n_split);
   CHECK(!fused_append(d, p));  // the wide kernel never appends
   const int64_t pos_off = kv_len - n_query;
+  const bool short_tile = wide2_short(gm, n_query);  // the waves past row 32 hold no live row
+  CHECK(!short_tile || (gm.NRT == 1 && 2 * n_query <= gm.BM));
   for (int64_t bid = 0; bid < gm.grid; ++bid) {
     int32_t gidx;
     int64_t work;
@@ -205,7 +207,7 @@ static void replay_wide2(const Dims& d, const Plan& p, int64_t kv_len, int64_t n
     for (int w = 0; w < kWideWaves; ++w) {
       int hw;
       int64_t off;
-      wide_wave(w, QT, d.HW, &hw, &off);
+      wide_wave(w, QT, d.HW, short_tile, &hw, &off);
       const int head = kvh * d.G + hq * d.HW + hw;
       CHECK(head >= 0 && head < d.Hq);
       for (int qt = 0; qt < QT; ++qt)

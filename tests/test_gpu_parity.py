@@ -70,6 +70,10 @@ CASES = {
     # wave per row (d = 128 and 64, bf16 and fp32)
     "many_rows_d64": W("many_rows_d64", 1, 16, 4, 64, 700, 256, 128, 70, 1, "bf16", seed=22),
     "f32_many_rows": W("f32_many_rows", 1, 8, 2, 64, 200, 64, 32, 130, 1, "f32", seed=23),
+    # a query step of at most half a query tile with four heads per workgroup
+    # (as the 1M workload's 32 query rows): the waves holding rows 32..63 only
+    # load tiles and meet barriers, and their SIMD partners do the arithmetic
+    "short_tile_g4": W("short_tile_g4", 1, 8, 2, 128, 2100, 512, 300, 24, 2, "bf16", seed=24),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
@@ -135,7 +139,7 @@ def test_phase2_query_and_decode_match_oracle(runs, name):
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g1_unaligned_a_lt_b", "g2_d64_wide_tail",
                                   "g8_narrow", "f32_gqa_d128", "long_tail_wide",
                                   "ragged_empty_split", "balanced_bnd", "balanced_b2_g8_d64",
-                                  "b1_a1", "ctx1", "b1_wide_tail", "f32_b1"])
+                                  "b1_a1", "ctx1", "b1_wide_tail", "f32_b1", "short_tile_g4"])
 def test_partials_are_the_hosts_replies(runs, name):
     """Each split's (vector, scalar) equals the oracle's host reply on that range."""
     p, _, _, _ = _pipeline(runs, name)
@@ -313,7 +317,7 @@ def test_binding_rejects_wrong_buffers():
                                   "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks",
                                   "balanced_bnd", "balanced_b2_g8_d64", "b1_a1", "ctx1",
                                   "f32_b1", "b1_wide_tail", "g2_d64_wide_tail", "long_tail_wide",
-                                  "kv_major_g8", "many_rows_d64"])
+                                  "kv_major_g8", "many_rows_d64", "short_tile_g4"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
     decode loop and against the three separate calls, every step: the query

@@ -55,6 +55,9 @@ def _shapes():
     lines.append(_line("many_groups", 8, 16, 8, 64, 2048, 512, 512, 40, 4))
     lines.append(_line("short_blocks", 1, 8, 2, 128, 70000, 100, 60, 5, 6))
     lines.append(_line("unaligned", 3, 12, 3, 128, 9001, 777, 333, 70, 9))
+    # query steps of at most half a query tile (four and two heads per workgroup)
+    lines.append(_line("short_tile_g4", 1, 8, 2, 128, 2100, 512, 300, 24, 2))
+    lines.append(_line("short_tile_g2", 2, 4, 2, 64, 3000, 700, 200, 40, 3))
     return "\n".join(lines) + "\n"
 
 
