@@ -390,6 +390,10 @@ def main():
     ap.add_argument("--seed", type=int, default=None,
                     help="seed of the synthetic inputs (default: the workload's, 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock record (about 1.5 s of back-to-back phase-1 launches "
+                         "after the timed steps), e.g. under a kernel trace whose per-kernel "
+                         "averages should cover the bench's own launches only")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the peak probes (libstarpeaks.so) run after the timed steps")
     ap.add_argument("--threads", type=int, default=None)
@@ -512,7 +516,8 @@ def main():
     bcfg = {"workload": args.workload, "paged": bool(args.paged), "rope": args.rope}
     t1, t2 = load_traffic(bcfg, kname1), load_traffic(bcfg, *kname2)
     # the shader clock phase 1 runs at (outside the timed region)
-    clock = gfx_clock_during(p.phase1 if rope is None else (lambda: p.phase1_rope(rope)), p1_ms)
+    clock = None if args.no_clock else gfx_clock_during(
+        p.phase1 if rope is None else (lambda: p.phase1_rope(rope)), p1_ms)
     # measured peaks (after the timed region): the rates each roofline is also
     # read against, beside the published peaks
     measured = None

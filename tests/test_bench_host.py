@@ -112,7 +112,7 @@ def test_flag_spellings_of_the_bench_record(monkeypatch, capsys):
     # --config, --reps and --seed are spellings the bench record documents;
     # --gpus above 1 stops before anything touches a GPU
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2", "--config", "llama8b_32k",
-                                     "--reps", "3", "--seed", "7"])
+                                     "--reps", "3", "--seed", "7", "--no-clock"])
     with pytest.raises(SystemExit) as e:
         bench.main()
     assert e.value.code == 2
