@@ -41,6 +41,9 @@ CASES = {
     # so the wide kernel keeps a kv head's work items on one XCD and reads
     # K/V with the default cache policy
     "kv_major_g8": W("kv_major", 2, 32, 4, 128, 640, 256, 256, 40, 1, "bf16", seed=21),
+    # a query step of at most half a query tile: the short-tile kernel, whose
+    # idle waves still load their share of every tile through the table
+    "short_tile_g4": W("short_tile_g4", 1, 8, 2, 128, 2100, 512, 300, 24, 2, "bf16", seed=24),
 }
 
 
