@@ -5,13 +5,17 @@
 //   attn_wide_kernel    flash-style bf16 MFMA tile loop shared by phase 1
 //                       (anchor pass + local causal pass, normalised bf16
 //                       output) and by phase-2 partials with many query rows
+//   attn_wide_short_kernel  the same phase-2 loop for a query tile at most
+//                       half full: the waves without live rows only load
+//                       tiles and meet barriers
 //   attn_decode_kernel  split-KV decode partials (<= 32 query columns), balanced
 //                       plan: one cache range per wave, no barriers
 //   attn_narrow_kernel  the same for the blockwise plan (blocks shorter than a
 //                       balanced range)
 //   attn_f32_kernel     fp32 path (VALU) for both phases
 //   lse_merge_kernel    exact softmax renormalisation of the partials (one
-//                       workgroup per output row)
+//                       workgroup per output row; lse_merge_rows_kernel: one
+//                       wave per row, for many rows)
 //
 // Method: Star Attention (hotaipapers.com summary page, podcast transcript,
 // Phase 1 and Phase 2 descriptions; paperhub.cn rebuttal, reply to reviewer
