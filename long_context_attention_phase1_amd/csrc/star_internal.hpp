@@ -217,6 +217,96 @@ STAR_HD static inline void wide_map(int64_t bid, bool phase1, int32_t NG, int32_
   }
 }
 
+// fp32 MFMA kernel: one wave (and workgroup) per 32 columns.
+// Phase 1: wave -> (sequence s, head h, row group rg); its columns are the
+// context rows 32 rg .. 32 rg + 31 of head h.
+STAR_HD static inline void f32m_phase1_map(int64_t wid, int64_t L, int32_t Hq, int64_t* s,
+                                           int32_t* h, int64_t* rg) {
+  const int64_t nrg = cdiv_hd(L, 32);
+  *rg = wid % nrg;
+  const int64_t t = wid / nrg;
+  *h = (int32_t)(t % Hq);
+  *s = t / Hq;
+}
+// Phase 2: wave -> (sequence s, kv head kvh, column group cg, split sigma);
+// column c of group cg is query row (32 cg + c) / G of head kvh * G + (32 cg + c) % G.
+STAR_HD static inline void f32m_phase2_map(int64_t wid, int32_t n_split, int64_t ncg, int32_t Hkv,
+                                           int64_t* s, int32_t* kvh, int64_t* cg,
+                                           int32_t* sigma) {
+  *sigma = (int32_t)(wid % n_split);
+  int64_t t = wid / n_split;
+  *cg = t % ncg;
+  t /= ncg;
+  *kvh = (int32_t)(t % Hkv);
+  *s = t / Hkv;
+}
+// Column c (0..31) of an fp32 MFMA wave: its row of q, head, whether it is a
+// live column, and the keys it sees: [0, hiA) and [loB, hiB) (phase 1: the
+// anchor for blocks >= 1, then its block causally; phase 2: split rows
+// [lo, hi) up to its own position). Phase 1: rg is the row group and h the
+// head; phase 2: cg is the column group and h the kv head.
+struct F32mCol {
+  int64_t row, hiA, loB, hiB;
+  int32_t head;
+  bool valid;
+};
+STAR_HD static inline F32mCol f32m_column(bool phase1, int c, int64_t rg_or_cg, int32_t h,
+                                          int64_t L, int64_t blk, int64_t anc, int64_t q_tokens,
+                                          int32_t G, int64_t kv_len, int64_t lo, int64_t hi) {
+  F32mCol x;
+  if (phase1) {
+    x.row = rg_or_cg * 32 + c;
+    x.head = h;
+    x.valid = x.row < L;
+    const int64_t i = x.valid ? x.row / blk : 0;
+    x.hiA = i > 0 ? anc : 0;
+    x.loB = i * blk;
+    x.hiB = x.row + 1;
+  } else {
+    const int64_t cc = rg_or_cg * 32 + c;
+    x.row = cc / G;
+    x.head = (int32_t)(h * G + cc % G);
+    x.valid = x.row < q_tokens;
+    const int64_t pos = kv_len - q_tokens + x.row;
+    x.hiA = 0;
+    x.loB = lo;
+    x.hiB = hi < pos + 1 ? hi : pos + 1;
+  }
+  return x;
+}
+// The keys an fp32 MFMA wave loads: [0, kA) and [kB0, kB1), the union of its
+// live columns' ranges; a 32-key slice [k0, k0 + 32) is processed when it
+// meets them (f32m_slice).
+STAR_HD static inline void f32m_wave_keys(bool phase1, int64_t rg_or_cg, int32_t h, int64_t L,
+                                          int64_t blk, int64_t anc, int64_t q_tokens, int32_t G,
+                                          int64_t kv_len, int64_t lo, int64_t hi, int64_t* kA,
+                                          int64_t* kB0, int64_t* kB1) {
+  *kA = 0;
+  *kB0 = INT64_MAX;
+  *kB1 = 0;
+  for (int c = 0; c < 32; ++c) {
+    const F32mCol x = f32m_column(phase1, c, rg_or_cg, h, L, blk, anc, q_tokens, G, kv_len, lo, hi);
+    if (!x.valid) continue;
+    if (x.hiA > *kA) *kA = x.hiA;
+    if (x.hiB > x.loB) {
+      if (x.loB < *kB0) *kB0 = x.loB;
+      if (x.hiB > *kB1) *kB1 = x.hiB;
+    }
+  }
+}
+STAR_HD static inline bool f32m_slice(int64_t k0, int64_t kA, int64_t kB0, int64_t kB1) {
+  return k0 < kA || (k0 + 32 > kB0 && k0 < kB1);
+}
+static inline int64_t f32m_ncg(const Dims& d, int64_t n_query) {
+  return cdiv_hd(n_query * d.G, 32);
+}
+static inline int64_t f32m_phase1_grid(const Dims& d) {
+  return (int64_t)d.B * d.Hq * cdiv_hd(d.L, 32);
+}
+static inline int64_t f32m_phase2_grid(const Dims& d, const Plan& p, int64_t n_query) {
+  return (int64_t)d.B * d.Hkv * f32m_ncg(d, n_query) * p.n_split;
+}
+
 // Phase 2 on the wide kernel: one query tile with at most half its rows live
 // (the waves holding the other half only load tiles and meet barriers).
 static inline bool wide2_short(const WideGeom& g, int64_t n_query) {
@@ -361,6 +451,7 @@ static inline int64_t kv_write_grid(const Dims& d, int64_t pos0, int64_t n_tok) 
 }
 
 // phase 1: bf16 wide kernel (512 threads), or one wave per column (fp32)
+// (fp32: the rotary path's one wave per column bounds the MFMA path's grid too)
 static inline bool phase1_fits(const Dims& d) {
   if (d.dtype == STAR_F32) return grid_fits(((int64_t)d.B * d.L * d.Hq + 3) / 4, 256);
   return grid_fits(phase1_geom(d).grid, 64 * kWideWaves);
@@ -368,7 +459,7 @@ static inline bool phase1_fits(const Dims& d) {
 
 // phase-2 partials under plan p
 static inline bool partial_fits(const Dims& d, const Plan& p, int64_t n_query) {
-  if (d.dtype == STAR_F32) return grid_fits(((int64_t)d.B * n_query * d.Hq * p.n_split + 3) / 4, 256);
+  if (d.dtype == STAR_F32) return grid_fits(f32m_phase2_grid(d, p, n_query), 64);
   if (p.narrow && p.balanced) {
     int32_t wpg;
     return grid_fits(decode_grid(d, p, &wpg), 256);

@@ -12,7 +12,9 @@
 //                       plan: one cache range per wave, no barriers
 //   attn_narrow_kernel  the same for the blockwise plan (blocks shorter than a
 //                       balanced range)
-//   attn_f32_kernel     fp32 path (VALU) for both phases
+//   attn_f32m_kernel    fp32 path on the matrix cores (v_mfma_f32_32x32x2_f32)
+//                       for phase 1 and the phase-2 partials
+//   attn_f32_kernel     fp32 phase 1 with a rotary embedding (VALU)
 //   lse_merge_kernel    exact softmax renormalisation of the partials (one
 //                       workgroup per output row; lse_merge_rows_kernel: one
 //                       wave per row, for many rows)
@@ -1801,6 +1803,150 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 on the matrix cores (phase 1 and phase-2 partials, no rotary
+// embedding): one wave per 32 columns, v_mfma_f32_32x32x2_f32 for both
+// products. Per 32-key slice the K rows and the V rows (turned back from the
+// transposed tile) are staged in LDS, rows outside the wave's key range zero;
+// S^T = K Q^T (A: K[key][2 ks + g], B: Q[column][2 ks + g]); each lane then
+// holds column l32 and keys 8 (r / 4) + 4 g + r % 4 of the slice; the online
+// softmax runs per column in fp32 (the lane pair l32, l32 + 32 shares a
+// column); P goes through LDS into the B layout of O^T += V^T P^T.
+// Phase 1: columns are 32 context rows of one head, each seeing the anchor
+// (blocks >= 1) and its own block causally. Phase 2: columns are (query row,
+// head) pairs of one kv head, each seeing split sigma's rows up to its own
+// position.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int acc_row(int r, int g) { return ((r >> 2) << 3) + (g << 2) + (r & 3); }
+
+template <int D, bool PHASE1, bool PAGED>
+__global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
+  static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
+  constexpr int DT = D / 32;  // O^T tiles of 32 dimensions
+  constexpr int LD = D + 1;   // padded LDS rows
+  __shared__ float sQ[32 * LD];
+  __shared__ float sK[32 * LD];
+  __shared__ float sV[32 * LD];
+  __shared__ float sP[32 * 33];
+  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+  const int64_t wid = blockIdx.x;
+
+  // the wave's columns: column c -> (token row in q, head), valid, and its
+  // visible keys: [0, hiA) (phase 1) and [loB, hiB) up to its position
+  int64_t s, ncg = 0, rg = 0, cg = 0;
+  int32_t h0 = 0, kvh, sigma = 0;
+  int64_t lo = 0, hi = 0;  // phase 2: the split's rows
+  if (PHASE1) {
+    f32m_phase1_map(wid, a.L, a.Hq, &s, &h0, &rg);
+    kvh = h0 / a.G;
+  } else {
+    ncg = cdiv_hd(a.q_tokens * a.G, 32);
+    f32m_phase2_map(wid, a.n_split, ncg, a.Hkv, &s, &kvh, &cg, &sigma);
+    int32_t host;
+    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len, sigma, &lo,
+               &hi, &host);
+  }
+  auto col = [&](int c) {
+    return f32m_column(PHASE1, c, PHASE1 ? rg : cg, PHASE1 ? h0 : kvh, a.L, a.blk, a.anc,
+                       a.q_tokens, a.G, a.kv_len, lo, hi);
+  };
+  // the wave's key range: the union of its columns' ranges (wave-uniform)
+  int64_t kA, kB0, kB1;
+  f32m_wave_keys(PHASE1, PHASE1 ? rg : cg, PHASE1 ? h0 : kvh, a.L, a.blk, a.anc, a.q_tokens, a.G,
+                 a.kv_len, lo, hi, &kA, &kB0, &kB1);
+  const int64_t head_row0 = (s * a.Hkv + kvh) * a.rows;
+  const float* K = PAGED ? a.k : a.k + head_row0 * D;
+  const float* V = PAGED ? a.v : a.v + head_row0 * D;
+  auto tile_at = [&](int64_t t) -> int64_t {
+    if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, (int)s, (int)kvh, t);
+    else return t * 64 * D;
+  };
+  // a key is loaded (else zero) if some column of the wave may see it
+  auto wanted = [&](int64_t key) { return key < kA || (key >= kB0 && key < kB1); };
+
+  // the columns' queries
+  for (int u = lane; u < 32 * D; u += 64) {
+    const int c = u / D, e = u % D;
+    const F32mCol x = col(c);
+    sQ[c * LD + e] = x.valid ? a.q[((s * a.q_tokens + x.row) * a.Hq + x.head) * D + e] : 0.0f;
+  }
+  const F32mCol me = col(l32);
+  float m = kMinit, l = 0.0f;
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+  const int64_t k_end = kA > kB1 ? kA : kB1;
+  for (int64_t k0 = 0; k0 < k_end; k0 += 32) {
+    if (!f32m_slice(k0, kA, kB0, kB1)) continue;  // no column sees this slice
+    __syncthreads();  // the previous slice's LDS reads are done
+    for (int u = lane; u < 32 * D; u += 64) {
+      const int kk = u / D, e = u % D;
+      const int64_t key = k0 + kk;
+      sK[kk * LD + e] = wanted(key) ? K[tile_at(key / 64) + (key % 64) * D + e] : 0.0f;
+      // V: consecutive lanes take consecutive keys of one dimension (V^T rows)
+      const int kv = u % 32, ev = u / 32;
+      const int64_t keyv = k0 + kv;
+      sV[kv * LD + ev] = wanted(keyv) ? V[tile_at(keyv / 64) + ev * 64 + (keyv % 64)] : 0.0f;
+    }
+    __syncthreads();
+    f32x16 sc = f32x16{};
+#pragma unroll 8
+    for (int ks = 0; ks < D / 2; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[l32 * LD + 2 * ks + g], sQ[l32 * LD + 2 * ks + g],
+                                                sc, 0, 0, 0);
+    float smax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = k0 + acc_row(r, g);
+      const bool vis = me.valid && (key < me.hiA || (key >= me.loB && key < me.hiB));
+      sc[r] = vis ? sc[r] * a.scale : -INFINITY;
+      smax = fmaxf(smax, sc[r]);
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+    const float m_new = fmaxf(m, smax);
+    const float alpha = expf(m - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = expf(sc[r] - m_new);  // 0 for a hidden key
+      psum += pr;
+      sP[acc_row(r, g) * 33 + l32] = pr;
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll 4
+      for (int kk = 0; kk < 16; ++kk)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[(2 * kk + g) * LD + 32 * dt + l32],
+                                                     sP[(2 * kk + g) * 33 + l32], o[dt], 0, 0, 0);
+  }
+
+  // O^T tile dt, element r of lane (l32, g): dimension 32 dt + acc_row(r, g) of column l32
+  if (!me.valid) return;
+  if (PHASE1) {
+    float* op = a.o + ((s * a.L + me.row) * a.Hq + me.head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) op[32 * dt + acc_row(r, g)] = o[dt][r] / l;
+  } else {
+    const int64_t b = ((s * a.q_tokens + me.row) * a.Hq + me.head) * a.n_split + sigma;
+    const bool any = l > 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        a.o_part[b * D + 32 * dt + acc_row(r, g)] = any ? o[dt][r] / l : 0.0f;
+    if (g == 0) a.lse_part[b] = any ? m + logf(l) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LSE merge: one workgroup per (sequence, query, head) row.
 // ---------------------------------------------------------------------------
 struct MergeArgs {
@@ -2053,9 +2199,17 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.q_tokens = d.L;
     a.n_cols = (int64_t)d.B * d.L * d.Hq;
     if (!grid_fits((a.n_cols + 3) / 4, 256)) return STAR_ERR_SHAPE;
-    const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false, ROPE>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, true, false, ROPE>), grid, dim3(256), 0, st, a);
+    if constexpr (ROPE == kRopeNone) {
+      // the matrix cores: one wave per 32 context rows of a head
+      const dim3 grid((unsigned)f32m_phase1_grid(d));
+      if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, true, false>), grid, dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((attn_f32m_kernel<64, true, false>), grid, dim3(64), 0, st, a);
+    } else {
+      // with a rotary embedding: one wave per column on the vector units
+      const dim3 grid((unsigned)((a.n_cols + 3) / 4));
+      if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false, ROPE>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((attn_f32_kernel<64, true, false, ROPE>), grid, dim3(256), 0, st, a);
+    }
     return check_launch();
   }
   WideArgs a{};
@@ -2165,10 +2319,12 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.per_block = p.per_block;
     a.n_split = p.n_split;
     a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
-    if (!grid_fits((a.n_cols + 3) / 4, 256)) return STAR_ERR_SHAPE;
-    const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, false, PAGED, kRopeNone>), grid, dim3(256), 0, st, a);
+    // the matrix cores: one wave per 32 (query row, head) columns of a kv head and split
+    const int64_t n = f32m_phase2_grid(d, p, n_query);
+    if (!grid_fits(n, 64)) return STAR_ERR_SHAPE;
+    const dim3 grid((unsigned)n);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32m_kernel<64, false, PAGED>), grid, dim3(64), 0, st, a);
     return check_launch();
   }
   if (p.narrow && p.balanced) {

@@ -16,7 +16,10 @@
 //     (sequence, query, head, split) partial is written exactly once; each
 //     split's rows are those the host-side plan gives it; every loaded row
 //     lies inside the cache and below kv_len; the appended rows of a fused
-//     decode step are written once.
+//     decode step are written once;
+//   * the fp32 kernel: every output or partial is written by one column of
+//     one wave, each column's keys are the method's key set, and every
+//     loaded slice lies inside the written cache rows.
 // No GPU; run by tests/test_work_coverage.py.
 #include <cstdint>
 #include <cstdio>
@@ -295,10 +298,73 @@ static void replay_narrow(const Dims& d, const Plan& p, int64_t kv_len, int64_t 
   CHECK(appended.dup == 0 && appended.set == appended.n);
 }
 
+// fp32 MFMA kernel: one wave per 32 columns (phase 1: rows of a head;
+// phase 2: (query, head) pairs of a kv head, one split)
+static void replay_f32m(const Dims& d, bool phase1, const Plan* p, int64_t kv_len,
+                        int64_t n_query) {
+  const int64_t q_tokens = phase1 ? d.L : n_query;
+  const int64_t ncg = phase1 ? 0 : f32m_ncg(d, n_query);
+  const int64_t grid = phase1 ? f32m_phase1_grid(d) : f32m_phase2_grid(d, *p, n_query);
+  const int64_t n_out = phase1 ? (int64_t)d.B * d.L * d.Hq
+                               : (int64_t)d.B * n_query * d.Hq * p->n_split;
+  const int64_t written = phase1 ? d.L : kv_len;
+  Bits outs(n_out);
+  for (int64_t wid = 0; wid < grid; ++wid) {
+    int64_t s, rg = 0, cg = 0, lo = 0, hi = 0;
+    int32_t h = 0, kvh = 0, sigma = 0;
+    if (phase1) {
+      f32m_phase1_map(wid, d.L, d.Hq, &s, &h, &rg);
+      kvh = h / d.G;
+    } else {
+      f32m_phase2_map(wid, p->n_split, ncg, d.Hkv, &s, &kvh, &cg, &sigma);
+      int32_t host;
+      split_rows(d.L, d.blk, d.n_blocks, p->per_block, p->blk_len, p->tail_len, kv_len, sigma, &lo,
+                 &hi, &host);
+      int64_t plo, phi;
+      plan_split(d, *p, kv_len, sigma, &plo, &phi);
+      CHECK(lo == plo && hi == phi);
+    }
+    CHECK(s >= 0 && s < d.B && kvh >= 0 && kvh < d.Hkv && sigma >= 0);
+    const int64_t gsel = phase1 ? rg : cg;
+    const int32_t hsel = phase1 ? h : kvh;
+    int64_t kA, kB0, kB1;
+    f32m_wave_keys(phase1, gsel, hsel, d.L, d.blk, d.anc, q_tokens, d.G, kv_len, lo, hi, &kA, &kB0,
+                   &kB1);
+    // the loaded rows: the wanted keys of the processed slices, all written
+    const int64_t k_end = kA > kB1 ? kA : kB1;
+    CHECK(kA <= written && kB1 <= written);
+    for (int64_t k0 = 0; k0 < k_end; k0 += 32)
+      if (f32m_slice(k0, kA, kB0, kB1)) check_tile(d, (int)s, kvh, k0 / 64);
+    for (int c = 0; c < 32; ++c) {
+      const F32mCol x = f32m_column(phase1, c, gsel, hsel, d.L, d.blk, d.anc, q_tokens, d.G,
+                                    kv_len, lo, hi);
+      if (!x.valid) continue;
+      CHECK(x.head >= 0 && x.head < d.Hq && x.head / d.G == kvh);
+      // the column's keys: the method's key set, inside the wave's loaded range
+      if (phase1) {
+        const int64_t i = x.row / d.blk;
+        CHECK(x.hiA == (i > 0 ? d.anc : 0) && x.loB == i * d.blk && x.hiB == x.row + 1);
+      } else {
+        const int64_t pos = kv_len - n_query + x.row;
+        CHECK(x.hiA == 0 && x.loB == lo && x.hiB == (hi < pos + 1 ? hi : pos + 1));
+      }
+      CHECK(x.hiA <= kA);
+      if (x.hiB > x.loB) CHECK(x.loB >= kB0 && x.hiB <= kB1);
+      outs.mark(phase1 ? (((int64_t)s * d.L + x.row) * d.Hq + x.head)
+                       : ((((int64_t)s * n_query + x.row) * d.Hq + x.head) * p->n_split + sigma));
+    }
+  }
+  CHECK(outs.dup == 0 && outs.set == outs.n);
+}
+
 static void replay_phase2(const Dims& d, int64_t kv_len, int64_t n_query, int64_t* count) {
   CHECK(validate_phase2(d, kv_len, n_query) == STAR_OK);
   const Plan p = make_plan(d, kv_len, n_query);
-  if (d.dtype != STAR_BF16) return;  // fp32 path: one wave per (column, split)
+  if (d.dtype != STAR_BF16) {
+    replay_f32m(d, false, &p, kv_len, n_query);
+    ++*count;
+    return;
+  }
   if (!p.narrow) replay_wide2(d, p, kv_len, n_query);
   else if (p.balanced) replay_decode(d, p, kv_len, n_query);
   else replay_narrow(d, p, kv_len, n_query);
@@ -328,6 +394,7 @@ int main() {
     if (g_fail) break;
     std::printf("%s\n", name);
     if (d.dtype == STAR_BF16) replay_phase1(d);
+    else replay_f32m(d, true, nullptr, 0, 0);
     // the query step, then decode steps: first, second, a middle one, last
     int64_t n2 = 0;
     replay_phase2(d, L + Tq, Tq, &n2);

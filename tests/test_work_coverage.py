@@ -58,6 +58,11 @@ def _shapes():
     # query steps of at most half a query tile (four and two heads per workgroup)
     lines.append(_line("short_tile_g4", 1, 8, 2, 128, 2100, 512, 300, 24, 2))
     lines.append(_line("short_tile_g2", 2, 4, 2, 64, 3000, 700, 200, 40, 3))
+    # fp32 shapes (the fp32 matrix-core kernel): ragged blocks, blocks shorter
+    # than a 32-row group, GQA, several column groups per kv head
+    lines.append(_line("f32_ragged", 2, 4, 2, 64, 333, 100, 37, 5, 2, f32=True))
+    lines.append(_line("f32_short_blocks", 1, 8, 2, 128, 200, 20, 7, 70, 3, f32=True))
+    lines.append(_line("f32_g1", 1, 3, 3, 64, 97, 97, 97, 40, 2, f32=True))
     return "\n".join(lines) + "\n"
 
 
