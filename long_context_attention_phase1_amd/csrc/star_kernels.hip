@@ -13,8 +13,8 @@
 //   attn_narrow_kernel  the same for the blockwise plan (blocks shorter than a
 //                       balanced range)
 //   attn_f32m_kernel    fp32 path on the matrix cores (v_mfma_f32_32x32x2_f32)
-//                       for phase 1 and the phase-2 partials
-//   attn_f32_kernel     fp32 phase 1 with a rotary embedding (VALU)
+//                       for phase 1 (with or without a rotary embedding) and
+//                       the phase-2 partials
 //   lse_merge_kernel    exact softmax renormalisation of the partials (one
 //                       workgroup per output row; lse_merge_rows_kernel: one
 //                       wave per row, for many rows)
@@ -1669,10 +1669,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const DecodeArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 path: one wave per (query column[, split]); lanes over keys for the
-// scores, lanes over dimensions for the output. Plain VALU arithmetic.
-// ---------------------------------------------------------------------------
+// fp32 path arguments (phase 1 and the phase-2 partials)
 struct F32Args {
   const float* k;
   const float* v;
@@ -1690,121 +1687,9 @@ struct F32Args {
   const float* rope_sin;
 };
 
-template <int D, bool PHASE1, bool PAGED, int ROPE>
-__global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
-  static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
-  static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
-  constexpr int E = D / 64;  // output dimensions per lane
-  __shared__ float qsm[4][D];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + w;
-  if (wid >= a.n_cols) return;
-  int64_t s, r, h, sigma = 0, pos;
-  int64_t loA = 0, hiA = 0, loB, hiB;
-  if (PHASE1) {
-    h = wid % a.Hq;
-    const int64_t t = wid / a.Hq;
-    r = t % a.L;
-    s = t / a.L;
-    const int64_t i = r / a.blk;
-    if (i > 0) hiA = a.anc;
-    loB = i * a.blk;
-    hiB = r + 1;
-    pos = r;
-  } else {
-    sigma = wid % a.n_split;
-    int64_t t = wid / a.n_split;
-    h = t % a.Hq;
-    t /= a.Hq;
-    r = t % a.q_tokens;
-    s = t / a.q_tokens;
-    int32_t host;
-    split_rows(a.L, a.blk, a.n_blocks, a.per_block, a.blk_len, a.tail_len, a.kv_len,
-               (int32_t)sigma, &loB, &hiB, &host);
-    pos = a.kv_len - a.q_tokens + r;
-    if (hiB > pos + 1) hiB = pos + 1;
-  }
-  const int64_t kvh = h / a.G;
-  const int64_t head_row0 = (s * a.Hkv + kvh) * a.rows;
-  const float* K = PAGED ? a.k : a.k + head_row0 * D;
-  const float* V = PAGED ? a.v : a.v + head_row0 * D;
-  // element offset of this (sequence, kv head)'s tile t from K and from V
-  auto tile_at = [&](int64_t t) -> int64_t {
-    if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, (int)s, (int)kvh, t);
-    else return t * 64 * D;
-  };
-  const float* qp = a.q + ((s * a.q_tokens + r) * a.Hq + h) * D;
-  // the query in LDS; with a rotary embedding, turned at position id pos
-  auto load_q = [&](int64_t qpos) {
-    if constexpr (ROPE != kRopeNone) {
-      for (int e = lane; e < D / 2; e += 64) {
-        const float x = qp[e], y = qp[e + D / 2];
-        const float c = a.rope_cos[qpos * (D / 2) + e], sn = a.rope_sin[qpos * (D / 2) + e];
-        qsm[w][e] = rope_a(x, y, c, sn);
-        qsm[w][e + D / 2] = rope_b(x, y, c, sn);
-      }
-    } else {
-      for (int e = lane; e < D; e += 64) qsm[w][e] = qp[e];
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  };
-  // adjacent anchor ids: the anchor pass turns the query back by i*b - a
-  const int64_t q_shift = (ROPE == kRopeAdjacent && PHASE1 && hiA > 0) ? (r / a.blk) * a.blk - a.anc : 0;
-  load_q(pos - q_shift);
-
-  float m = kMinit, l = 0.0f, o[E];
-#pragma unroll
-  for (int j = 0; j < E; ++j) o[j] = 0.0f;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int64_t lo = pass == 0 ? loA : loB, hi = pass == 0 ? hiA : hiB;
-    if (ROPE == kRopeAdjacent && pass == 1 && q_shift != 0) {
-      __builtin_amdgcn_wave_barrier();  // every lane's reads of the anchor pass are done
-      load_q(pos);
-    }
-    for (int64_t base = lo; base < hi; base += 64) {
-      const int64_t key = base + lane;
-      const bool ok = key < hi;
-      float sc = -INFINITY;
-      if (ok) {
-        const float* kp = K + tile_at(key / 64) + (key % 64) * D;
-        float dot = 0.0f;
-        for (int e = 0; e < D; ++e) dot = fmaf(qsm[w][e], kp[e], dot);
-        sc = dot * a.scale;
-      }
-      const float m_new = fmaxf(m, wave_max(sc));
-      const float alpha = expf(m - m_new);
-      const float p = ok ? expf(sc - m_new) : 0.0f;
-      l = l * alpha + wave_sum(p);
-#pragma unroll
-      for (int j = 0; j < E; ++j) o[j] *= alpha;
-      m = m_new;
-      const int64_t cnt = hi - base < 64 ? hi - base : 64;
-      for (int kk = 0; kk < cnt; ++kk) {
-        const float pk = __shfl(p, kk, 64);
-        const int64_t kr = base + kk;
-        const float* vt = V + tile_at(kr / 64) + (kr % 64);
-#pragma unroll
-        for (int j = 0; j < E; ++j) o[j] = fmaf(pk, vt[(lane + 64 * j) * 64], o[j]);
-      }
-    }
-  }
-  if (PHASE1) {
-    float* op = a.o + ((s * a.L + r) * a.Hq + h) * D;
-#pragma unroll
-    for (int j = 0; j < E; ++j) op[lane + 64 * j] = o[j] / l;
-  } else {
-    const int64_t b = ((s * a.q_tokens + r) * a.Hq + h) * a.n_split + sigma;
-    const bool any = l > 0.0f;
-#pragma unroll
-    for (int j = 0; j < E; ++j) a.o_part[b * D + lane + 64 * j] = any ? o[j] / l : 0.0f;
-    if (lane == 0) a.lse_part[b] = any ? m + logf(l) : -INFINITY;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// fp32 on the matrix cores (phase 1 and phase-2 partials, no rotary
-// embedding): one wave per 32 columns, v_mfma_f32_32x32x2_f32 for both
+// fp32 on the matrix cores (phase 1, with or without a rotary embedding, and
+// the phase-2 partials): one wave per 32 columns, v_mfma_f32_32x32x2_f32 for both
 // products. Per 32-key slice the K rows and the V rows (turned back from the
 // transposed tile) are staged in LDS, rows outside the wave's key range zero;
 // S^T = K Q^T (A: K[key][2 ks + g], B: Q[column][2 ks + g]); each lane then
@@ -1818,12 +1703,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const F32Args a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int acc_row(int r, int g) { return ((r >> 2) << 3) + (g << 2) + (r & 3); }
 
-template <int D, bool PHASE1, bool PAGED>
+template <int D, bool PHASE1, bool PAGED, int ROPE>
 __global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
+  static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   constexpr int DT = D / 32;  // O^T tiles of 32 dimensions
   constexpr int LD = D + 1;   // padded LDS rows
+  constexpr bool ADJ = ROPE == kRopeAdjacent;
   __shared__ float sQ[32 * LD];
+  __shared__ float sQa[ADJ ? 32 * LD : 1];  // adjacent ids: the query turned back for the anchor
   __shared__ float sK[32 * LD];
   __shared__ float sV[32 * LD];
   __shared__ float sP[32 * 33];
@@ -1863,11 +1751,31 @@ __global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
   // a key is loaded (else zero) if some column of the wave may see it
   auto wanted = [&](int64_t key) { return key < kA || (key >= kB0 && key < kB1); };
 
-  // the columns' queries
+  // the columns' queries; with a rotary embedding turned at the column's
+  // position id (pairs e, e + D/2), and for adjacent anchor ids also turned
+  // back by i*b - a for the anchor's keys (rotations compose: the cached
+  // anchor keys stay at their own row ids)
   for (int u = lane; u < 32 * D; u += 64) {
     const int c = u / D, e = u % D;
     const F32mCol x = col(c);
-    sQ[c * LD + e] = x.valid ? a.q[((s * a.q_tokens + x.row) * a.Hq + x.head) * D + e] : 0.0f;
+    float vb = 0.0f, va = 0.0f;
+    if (x.valid) {
+      const float* qp = a.q + ((s * a.q_tokens + x.row) * a.Hq + x.head) * D;
+      if constexpr (ROPE == kRopeNone) {
+        vb = qp[e];
+      } else {
+        const int e2 = e < D / 2 ? e : e - D / 2;
+        const float qx = qp[e2], qy = qp[e2 + D / 2];
+        auto turn = [&](int64_t id) {
+          const float cc = a.rope_cos[id * (D / 2) + e2], sn = a.rope_sin[id * (D / 2) + e2];
+          return e < D / 2 ? rope_a(qx, qy, cc, sn) : rope_b(qx, qy, cc, sn);
+        };
+        vb = turn(x.row);
+        if constexpr (ADJ) va = turn(x.hiA > 0 ? x.row - ((x.row / a.blk) * a.blk - a.anc) : x.row);
+      }
+    }
+    sQ[c * LD + e] = vb;
+    if constexpr (ADJ) sQa[c * LD + e] = va;
   }
   const F32mCol me = col(l32);
   float m = kMinit, l = 0.0f;
@@ -1894,6 +1802,18 @@ __global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
     for (int ks = 0; ks < D / 2; ++ks)
       sc = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[l32 * LD + 2 * ks + g], sQ[l32 * LD + 2 * ks + g],
                                                 sc, 0, 0, 0);
+    if constexpr (ADJ) {
+      if (k0 < kA) {  // anchor keys of blocks >= 1: scores with the turned-back query
+        f32x16 sa = f32x16{};
+#pragma unroll 8
+        for (int ks = 0; ks < D / 2; ++ks)
+          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[l32 * LD + 2 * ks + g],
+                                                    sQa[l32 * LD + 2 * ks + g], sa, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (k0 + acc_row(r, g) < me.hiA) sc[r] = sa[r];
+      }
+    }
     float smax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -2198,18 +2118,11 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.rope_sin = rope_sin;
     a.q_tokens = d.L;
     a.n_cols = (int64_t)d.B * d.L * d.Hq;
-    if (!grid_fits((a.n_cols + 3) / 4, 256)) return STAR_ERR_SHAPE;
-    if constexpr (ROPE == kRopeNone) {
-      // the matrix cores: one wave per 32 context rows of a head
-      const dim3 grid((unsigned)f32m_phase1_grid(d));
-      if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, true, false>), grid, dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((attn_f32m_kernel<64, true, false>), grid, dim3(64), 0, st, a);
-    } else {
-      // with a rotary embedding: one wave per column on the vector units
-      const dim3 grid((unsigned)((a.n_cols + 3) / 4));
-      if (d.D == 128) hipLaunchKernelGGL((attn_f32_kernel<128, true, false, ROPE>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((attn_f32_kernel<64, true, false, ROPE>), grid, dim3(256), 0, st, a);
-    }
+    // the matrix cores: one wave per 32 context rows of a head
+    if (!grid_fits(f32m_phase1_grid(d), 64)) return STAR_ERR_SHAPE;
+    const dim3 grid((unsigned)f32m_phase1_grid(d));
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, true, false, ROPE>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32m_kernel<64, true, false, ROPE>), grid, dim3(64), 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -2323,8 +2236,8 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     const int64_t n = f32m_phase2_grid(d, p, n_query);
     if (!grid_fits(n, 64)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)n);
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32m_kernel<64, false, PAGED>), grid, dim3(64), 0, st, a);
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED, kRopeNone>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((attn_f32m_kernel<64, false, PAGED, kRopeNone>), grid, dim3(64), 0, st, a);
     return check_launch();
   }
   if (p.narrow && p.balanced) {
