@@ -1677,7 +1677,7 @@ struct F32Args {
   float* o;
   float* o_part;
   float* lse_part;
-  int64_t rows, q_tokens, L, blk, anc, kv_len, n_cols;
+  int64_t rows, q_tokens, L, blk, anc, kv_len;
   int64_t blk_len, tail_len;
   int32_t per_block, n_split, n_blocks;
   int32_t Hq, Hkv, G;
@@ -2117,7 +2117,6 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     a.q_tokens = d.L;
-    a.n_cols = (int64_t)d.B * d.L * d.Hq;
     // the matrix cores: one wave per 32 context rows of a head
     if (!grid_fits(f32m_phase1_grid(d), 64)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)f32m_phase1_grid(d));
@@ -2231,7 +2230,6 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.tail_len = p.tail_len;
     a.per_block = p.per_block;
     a.n_split = p.n_split;
-    a.n_cols = (int64_t)d.B * n_query * d.Hq * p.n_split;
     // the matrix cores: one wave per 32 (query row, head) columns of a kv head and split
     const int64_t n = f32m_phase2_grid(d, p, n_query);
     if (!grid_fits(n, 64)) return STAR_ERR_SHAPE;
