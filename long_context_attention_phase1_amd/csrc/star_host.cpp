@@ -108,7 +108,10 @@ Plan make_plan(const Dims& d, int64_t kv_len, int64_t n_query) {
   // splits cost more partial traffic than they gain in balance (the 128K
   // query step: 0.33 ms at 257 splits per kv head, 0.21 ms at 33)
   const int64_t total = p.narrow ? kNarrowWorkgroups : kTargetWorkgroups;
-  const int64_t min_len = p.narrow ? 512 : 256;
+  // fp32: one wave runs a split's 32-key slices one after another at the
+  // matrix core's rate, so splits as short as a tile keep a short step's
+  // chains parallel
+  const int64_t min_len = d.dtype != STAR_BF16 ? kTile : (p.narrow ? 512 : 256);
   int64_t target = total / ((int64_t)p.n_groups * p.n_qtiles);
   if (target < 1) target = 1;
   // splits per context block: proportional to the block's share of the cache,

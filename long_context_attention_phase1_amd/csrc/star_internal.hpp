@@ -297,6 +297,27 @@ STAR_HD static inline void f32m_wave_keys(bool phase1, int64_t rg_or_cg, int32_t
 STAR_HD static inline bool f32m_slice(int64_t k0, int64_t kA, int64_t kB0, int64_t kB1) {
   return k0 < kA || (k0 + 32 > kB0 && k0 < kB1);
 }
+// The same slices in closed form, in order: the nA slices of [0, kA), then
+// the block slices from bf up to kB1; slice i starts at f32m_slice_at(i).
+struct F32mSlices {
+  int64_t nA, bf, n;
+};
+STAR_HD static inline F32mSlices f32m_slices(int64_t kA, int64_t kB0, int64_t kB1) {
+  F32mSlices r;
+  r.nA = cdiv_hd(kA, 32);
+  const bool any_b = kB1 > kB0;
+  const int64_t bl = any_b ? cdiv_hd(kB1, 32) : 0;
+  r.bf = any_b ? kB0 / 32 : 0;
+  if (r.bf < r.nA) r.bf = r.nA;
+  r.n = r.nA + (bl > r.bf ? bl - r.bf : 0);
+  return r;
+}
+STAR_HD static inline int64_t f32m_slice_at(const F32mSlices& sl, int64_t i) {
+  return 32 * (i < sl.nA ? i : sl.bf + (i - sl.nA));
+}
+// Waves per fp32 workgroup: its 32 columns' slices are dealt round robin to
+// them (the LDS holds a K, V and P buffer per wave).
+STAR_HD constexpr int f32m_waves(int D) { return D <= 64 ? 4 : 2; }
 static inline int64_t f32m_ncg(const Dims& d, int64_t n_query) {
   return cdiv_hd(n_query * d.G, 32);
 }
@@ -450,16 +471,15 @@ static inline int64_t kv_write_grid(const Dims& d, int64_t pos0, int64_t n_tok) 
   return ((pos0 + n_tok - 1) / kTile - pos0 / kTile + 1) * d.B * d.Hkv;
 }
 
-// phase 1: bf16 wide kernel (512 threads), or one wave per column (fp32)
-// (fp32: the rotary path's one wave per column bounds the MFMA path's grid too)
+// phase 1: bf16 wide kernel (512 threads), or one wave per 32 rows of a head (fp32)
 static inline bool phase1_fits(const Dims& d) {
-  if (d.dtype == STAR_F32) return grid_fits(((int64_t)d.B * d.L * d.Hq + 3) / 4, 256);
+  if (d.dtype == STAR_F32) return grid_fits(f32m_phase1_grid(d), 64 * f32m_waves(d.D));
   return grid_fits(phase1_geom(d).grid, 64 * kWideWaves);
 }
 
 // phase-2 partials under plan p
 static inline bool partial_fits(const Dims& d, const Plan& p, int64_t n_query) {
-  if (d.dtype == STAR_F32) return grid_fits(f32m_phase2_grid(d, p, n_query), 64);
+  if (d.dtype == STAR_F32) return grid_fits(f32m_phase2_grid(d, p, n_query), 64 * f32m_waves(d.D));
   if (p.narrow && p.balanced) {
     int32_t wpg;
     return grid_fits(decode_grid(d, p, &wpg), 256);

@@ -1703,19 +1703,32 @@ struct F32Args {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int acc_row(int r, int g) { return ((r >> 2) << 3) + (g << 2) + (r & 3); }
 
+// Bit j set for the keys k0 + j (j < 32) that lie in [lo, hi).
+__device__ __forceinline__ uint32_t range_bits(int64_t lo, int64_t hi, int64_t k0) {
+  const int64_t a = lo - k0 < 0 ? 0 : (lo - k0 > 32 ? 32 : lo - k0);
+  const int64_t b = hi - k0 < 0 ? 0 : (hi - k0 > 32 ? 32 : hi - k0);
+  const uint32_t below_b = b >= 32 ? 0xFFFFFFFFu : (1u << b) - 1u;
+  const uint32_t below_a = a >= 32 ? 0xFFFFFFFFu : (1u << a) - 1u;
+  return b > a ? below_b & ~below_a : 0u;
+}
+
 template <int D, bool PHASE1, bool PAGED, int ROPE>
-__global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
+__global__ __launch_bounds__(64 * f32m_waves(D)) void attn_f32m_kernel(const F32Args a) {
   static_assert(!(PHASE1 && PAGED), "phase 1 reads the contiguous cache");
   static_assert(PHASE1 || ROPE == kRopeNone, "rotary embedding is fused into phase 1");
   constexpr int DT = D / 32;  // O^T tiles of 32 dimensions
   constexpr int LD = D + 1;   // padded LDS rows
   constexpr bool ADJ = ROPE == kRopeAdjacent;
+  constexpr int NW = f32m_waves(D);  // waves; slice i of the workgroup goes to wave i % NW
   __shared__ float sQ[32 * LD];
   __shared__ float sQa[ADJ ? 32 * LD : 1];  // adjacent ids: the query turned back for the anchor
-  __shared__ float sK[32 * LD];
-  __shared__ float sV[32 * LD];
-  __shared__ float sP[32 * 33];
-  const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+  __shared__ float sKw[NW * 32 * LD];       // per wave: K rows, V^T rows, P
+  __shared__ float sVw[NW * 32 * LD];
+  __shared__ float sPw[NW * 32 * 33];
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5, w = threadIdx.x >> 6;
+  float* const sK = sKw + w * 32 * LD;
+  float* const sV = sVw + w * 32 * LD;
+  float* const sP = sPw + w * 32 * 33;
   const int64_t wid = blockIdx.x;
 
   // the wave's columns: column c -> (token row in q, head), valid, and its
@@ -1748,16 +1761,36 @@ __global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
     if constexpr (PAGED) return tile_elem<true, D>(a.pm, a.rows, a.Hkv, (int)s, (int)kvh, t);
     else return t * 64 * D;
   };
-  // a key is loaded (else zero) if some column of the wave may see it
-  auto wanted = [&](int64_t key) { return key < kA || (key >= kB0 && key < kB1); };
+  // the keys of slice [k0, k0 + 32) that are loaded (else zero): those some
+  // column of the wave may see, as a bit mask
+  auto slice_bits = [&](int64_t k0) { return range_bits(0, kA, k0) | range_bits(kB0, kB1, k0); };
+  // x, or +0 where bit j of m is clear, on the bits: the pieces hold the
+  // unwritten (possibly NaN) rows next to wanted keys, and a floating-point
+  // select of a NaN is not something the no-NaN build may keep
+  auto keep = [](float x, uint32_t m, int j) {
+    return __uint_as_float(__float_as_uint(x) & (0u - ((m >> j) & 1u)));
+  };
 
   // the columns' queries; with a rotary embedding turned at the column's
   // position id (pairs e, e + D/2), and for adjacent anchor ids also turned
   // back by i*b - a for the anchor's keys (rotations compose: the cached
   // anchor keys stay at their own row ids)
-  for (int u = lane; u < 32 * D; u += 64) {
-    const int c = u / D, e = u % D;
-    const F32mCol x = col(c);
+  // Each lane works out its own column once (the map divides by the block
+  // length); an iteration's column c is the same on every lane, so its fields
+  // come from lane c by readlane.
+  const F32mCol me = col(l32);
+  auto from_lane = [](int64_t v, int c) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, c);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), c);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  for (int k = w; k < 32 * D / 64; k += NW) {  // the waves share the staging
+    const int c = 64 * k / D, e = (lane + 64 * k) % D;  // element u = lane + 64 k: column u / D
+    F32mCol x;
+    x.valid = __builtin_amdgcn_readlane((int)me.valid, c) != 0;
+    x.row = from_lane(me.row, c);
+    x.head = __builtin_amdgcn_readlane(me.head, c);
+    x.hiA = from_lane(me.hiA, c);
     float vb = 0.0f, va = 0.0f;
     if (x.valid) {
       const float* qp = a.q + ((s * a.q_tokens + x.row) * a.Hq + x.head) * D;
@@ -1777,73 +1810,177 @@ __global__ __launch_bounds__(64) void attn_f32m_kernel(const F32Args a) {
     sQ[c * LD + e] = vb;
     if constexpr (ADJ) sQa[c * LD + e] = va;
   }
-  const F32mCol me = col(l32);
+  __syncthreads();
+  // d = 64: the B operands of S^T = K Q^T stay in registers for the whole
+  // loop; d = 128 reads them from LDS with the K operands (registers would
+  // spill next to the slice prefetch)
+  constexpr bool QREG = D <= 64;
+  float qop[QREG ? D / 2 : 1], qaop[QREG && ADJ ? D / 2 : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) {
+      qop[ks] = sQ[l32 * LD + 2 * ks + g];
+      if constexpr (ADJ) qaop[ks] = sQa[l32 * LD + 2 * ks + g];
+    }
+  }
+  // 16 k-steps of S^T from K and the query copy qs (registers qr or LDS)
+  auto qk16 = [&](f32x16 acc, int k16, const float* qr, const float* qs) {
+    float kop[16], qch[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      kop[j] = sK[l32 * LD + 2 * (16 * k16 + j) + g];
+      qch[j] = QREG ? qr[16 * k16 + j] : qs[l32 * LD + 2 * (16 * k16 + j) + g];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[j], qch[j], acc, 0, 0, 0);
+    return acc;
+  };
   float m = kMinit, l = 0.0f;
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  const int64_t k_end = kA > kB1 ? kA : kB1;
-  for (int64_t k0 = 0; k0 < k_end; k0 += 32) {
-    if (!f32m_slice(k0, kA, kB0, kB1)) continue;  // no column sees this slice
-    __syncthreads();  // the previous slice's LDS reads are done
-    for (int u = lane; u < 32 * D; u += 64) {
-      const int kk = u / D, e = u % D;
-      const int64_t key = k0 + kk;
-      sK[kk * LD + e] = wanted(key) ? K[tile_at(key / 64) + (key % 64) * D + e] : 0.0f;
-      // V: consecutive lanes take consecutive keys of one dimension (V^T rows)
-      const int kv = u % 32, ev = u / 32;
-      const int64_t keyv = k0 + kv;
-      sV[kv * LD + ev] = wanted(keyv) ? V[tile_at(keyv / 64) + ev * 64 + (keyv % 64)] : 0.0f;
-    }
-    __syncthreads();
-    f32x16 sc = f32x16{};
-#pragma unroll 8
-    for (int ks = 0; ks < D / 2; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[l32 * LD + 2 * ks + g], sQ[l32 * LD + 2 * ks + g],
-                                                sc, 0, 0, 0);
-    if constexpr (ADJ) {
-      if (k0 < kA) {  // anchor keys of blocks >= 1: scores with the turned-back query
-        f32x16 sa = f32x16{};
-#pragma unroll 8
-        for (int ks = 0; ks < D / 2; ++ks)
-          sa = __builtin_amdgcn_mfma_f32_32x32x2f32(sK[l32 * LD + 2 * ks + g],
-                                                    sQa[l32 * LD + 2 * ks + g], sa, 0, 0, 0);
+  // A slice's K and V go through registers in 16-byte pieces: all of a
+  // slice's loads are issued one slice ahead, so they land during the
+  // arithmetic of the slice before. Piece f = lane + 64 i of K is key f/(D/4),
+  // dimensions 4 (f % (D/4)) + 0..3; piece f of V^T is dimension f / 8, keys
+  // 4 (f % 8) + 0..3. A piece whose keys no column sees reads row 0 (always
+  // written); every element of a key no column sees is stored as zero.
+  constexpr int NF = D / 8;  // pieces of each matrix per lane
+  f32x4 kr[NF], vr[NF];
+  // a slice lies inside one 64-key tile: its K rows and V^T columns start at
+  // one base each; a piece no column wants reads tile 0 (row 0 is written)
+  const float* const K0 = K + tile_at(0);
+  const float* const V0 = V + tile_at(0);
+  auto fetch = [&](int64_t k0) {
+    const uint32_t wm = slice_bits(k0);
+    const int64_t t = tile_at(k0 / 64);
+    const float* const Kb = K + t + (k0 % 64) * D;
+    const float* const Vb = V + t + (k0 % 64);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + acc_row(r, g) < me.hiA) sc[r] = sa[r];
+    for (int i = 0; i < NF; ++i) {
+      const int f = lane + 64 * i;
+      const int j = f / (D / 4), e = 4 * (f % (D / 4));
+      kr[i] = *(const f32x4*)(((wm >> j) & 1u) ? Kb + j * D + e : K0 + e);
+      const int dv = f / 8, kq = 4 * (f % 8);
+      vr[i] = *(const f32x4*)(((wm >> kq) & 15u) ? Vb + dv * 64 + kq : V0 + dv * 64);
+    }
+  };
+  // the workgroup's slices (those some column sees), dealt round robin to
+  // the waves; every wave meets every barrier of the rounds
+  const F32mSlices sl = f32m_slices(kA, kB0, kB1);
+  const int64_t rounds = cdiv_hd(sl.n, NW);
+  if (w < sl.n) fetch(f32m_slice_at(sl, w));
+  for (int64_t rd = 0, si = w; rd < rounds; ++rd, si += NW) {
+    const bool act = si < sl.n;
+    const int64_t k0 = act ? f32m_slice_at(sl, si) : 0;
+    __syncthreads();  // the previous slice's LDS reads are done
+    if (act) {
+      const uint32_t wm = slice_bits(k0);
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const int f = lane + 64 * i;
+        const int kk = f / (D / 4), e = 4 * (f % (D / 4));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sK[kk * LD + e + c] = keep(kr[i][c], wm, kk);
+        const int ev = f / 8, kv = 4 * (f % 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sV[(kv + c) * LD + ev] = keep(vr[i][c], wm, kv + c);
       }
     }
-    float smax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t key = k0 + acc_row(r, g);
-      const bool vis = me.valid && (key < me.hiA || (key >= me.loB && key < me.hiB));
-      sc[r] = vis ? sc[r] * a.scale : -INFINITY;
-      smax = fmaxf(smax, sc[r]);
-    }
-    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-    const float m_new = fmaxf(m, smax);
-    const float alpha = expf(m - m_new);
-    float psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = expf(sc[r] - m_new);  // 0 for a hidden key
-      psum += pr;
-      sP[acc_row(r, g) * 33 + l32] = pr;
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     __syncthreads();
+    if (si + NW < sl.n) fetch(f32m_slice_at(sl, si + NW));
+    if (act) {  // (a wave with no slice this round only meets the barriers)
+      // the operands are read 16 k-steps ahead of their MFMAs
+      f32x16 sc = f32x16{};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll 4
-      for (int kk = 0; kk < 16; ++kk)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[(2 * kk + g) * LD + 32 * dt + l32],
-                                                     sP[(2 * kk + g) * 33 + l32], o[dt], 0, 0, 0);
+      for (int k16 = 0; k16 < D / 32; ++k16) sc = qk16(sc, k16, qop, sQ);
+      if constexpr (ADJ) {
+        if (k0 < kA) {  // anchor keys of blocks >= 1: scores with the turned-back query
+          f32x16 sa = f32x16{};
+#pragma unroll
+          for (int k16 = 0; k16 < D / 32; ++k16) sa = qk16(sa, k16, qaop, sQa);
+          const uint32_t am = range_bits(0, me.hiA, k0) >> (4 * g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((am >> acc_row(r, 0)) & 1u) sc[r] = sa[r];
+        }
+      }
+      // the keys of this slice the lane's column sees; element r holds key
+      // k0 + acc_row(r, g) = k0 + acc_row(r, 0) + 4 g
+      const uint32_t cm =
+          (me.valid ? range_bits(0, me.hiA, k0) | range_bits(me.loB, me.hiB, k0) : 0u) >> (4 * g);
+      float smax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = (cm >> acc_row(r, 0)) & 1u;
+        sc[r] = vis ? sc[r] * a.scale : -INFINITY;
+        smax = fmaxf(smax, sc[r]);
+      }
+      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      const float m_new = fmaxf(m, smax);
+      const float alpha = expf(m - m_new);
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = expf(sc[r] - m_new);  // 0 for a hidden key
+        psum += pr;
+        sP[acc_row(r, g) * 33 + l32] = pr;
+      }
+      psum += __shfl_xor(psum, 32, 64);
+      l = l * alpha + psum;
+      m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    __syncthreads();
+    if (act) {
+      // P and V operands, read ahead of their MFMAs (V one O^T tile at a time)
+      float pop[16];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) pop[kk] = sP[(2 * kk + g) * 33 + l32];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        float vop[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) vop[kk] = sV[(2 * kk + g) * LD + 32 * dt + l32];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop[kk], pop[kk], o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // The waves' states (m, l, O^T over disjoint slices) merge exactly: wave
+  // w > 0 leaves them in its own buffers, wave 0 rescales to the common max.
+  if constexpr (NW > 1) {
+    __syncthreads();
+    if (w > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sK[l32 * LD + 32 * dt + acc_row(r, g)] = o[dt][r];
+      if (g == 0) {
+        sP[l32] = m;
+        sP[32 + l32] = l;
+      }
+    }
+    __syncthreads();
+    if (w > 0) return;
+    for (int v = 1; v < NW; ++v) {
+      const float* xo = sKw + v * 32 * LD;
+      const float* xs = sPw + v * 32 * 33;
+      const float mv = xs[l32], lv = xs[32 + l32];
+      const float mn = fmaxf(m, mv);
+      const float a0 = expf(m - mn), a1 = expf(mv - mn);
+      l = l * a0 + lv * a1;
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[dt][r] = o[dt][r] * a0 + xo[l32 * LD + 32 * dt + acc_row(r, g)] * a1;
+    }
   }
 
   // O^T tile dt, element r of lane (l32, g): dimension 32 dt + acc_row(r, g) of column l32
@@ -2118,10 +2255,11 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.rope_sin = rope_sin;
     a.q_tokens = d.L;
     // the matrix cores: one wave per 32 context rows of a head
-    if (!grid_fits(f32m_phase1_grid(d), 64)) return STAR_ERR_SHAPE;
+    if (!grid_fits(f32m_phase1_grid(d), 64 * f32m_waves(d.D))) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)f32m_phase1_grid(d));
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, true, false, ROPE>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32m_kernel<64, true, false, ROPE>), grid, dim3(64), 0, st, a);
+    const dim3 block((unsigned)(64 * f32m_waves(d.D)));
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, true, false, ROPE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_f32m_kernel<64, true, false, ROPE>), grid, block, 0, st, a);
     return check_launch();
   }
   WideArgs a{};
@@ -2234,8 +2372,9 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     const int64_t n = f32m_phase2_grid(d, p, n_query);
     if (!grid_fits(n, 64)) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)n);
-    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED, kRopeNone>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_f32m_kernel<64, false, PAGED, kRopeNone>), grid, dim3(64), 0, st, a);
+    const dim3 block((unsigned)(64 * f32m_waves(d.D)));
+    if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED, kRopeNone>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_f32m_kernel<64, false, PAGED, kRopeNone>), grid, block, 0, st, a);
     return check_launch();
   }
   if (p.narrow && p.balanced) {

@@ -333,8 +333,22 @@ static void replay_f32m(const Dims& d, bool phase1, const Plan* p, int64_t kv_le
     // the loaded rows: the wanted keys of the processed slices, all written
     const int64_t k_end = kA > kB1 ? kA : kB1;
     CHECK(kA <= written && kB1 <= written);
-    for (int64_t k0 = 0; k0 < k_end; k0 += 32)
-      if (f32m_slice(k0, kA, kB0, kB1)) check_tile(d, (int)s, kvh, k0 / 64);
+    // the closed-form slice list is exactly the slices f32m_slice accepts, in
+    // order, and the round-robin deal gives each to one wave
+    const F32mSlices sl = f32m_slices(kA, kB0, kB1);
+    const int NW = f32m_waves(d.D);
+    int64_t n_seen = 0;
+    for (int64_t k0 = 0; k0 < k_end; k0 += 32) {
+      if (!f32m_slice(k0, kA, kB0, kB1)) continue;
+      CHECK(n_seen < sl.n && f32m_slice_at(sl, n_seen) == k0);
+      check_tile(d, (int)s, kvh, k0 / 64);
+      ++n_seen;
+    }
+    CHECK(n_seen == sl.n);
+    int64_t dealt = 0;
+    for (int w = 0; w < NW; ++w)
+      for (int64_t si = w; si < sl.n; si += NW) ++dealt;
+    CHECK(dealt == sl.n);
     for (int c = 0; c < 32; ++c) {
       const F32mCol x = f32m_column(phase1, c, gsel, hsel, d.L, d.blk, d.anc, q_tokens, d.G,
                                     kv_len, lo, hi);
