@@ -8,12 +8,14 @@ autoregressive decode loop (n_decode steps of append + partials + merge).
 Prints ONE JSON line. ``value`` is the phase-1 context throughput (tokens/s)
 measured inside the timed steps; the decode figure (µs per step and per
 token) is reported beside it. ``roofline`` is for the dominant kernel
-(phase 1, MFMA-bound), from HIP events recorded on the launch stream around
-every phase-1 launch in the timed steps; ``roofline_query`` is for the
-query step against the larger of its two bounds; ``roofline_phase2`` is for the
-decode step (HBM-bound), from events around the whole decode loop (every
-step's two launches: append + partials, merge) divided by the steps. ``cpu_baseline`` is the fp64 oracle timed on a bounded
-sample on the host.
+(phase 1, MFMA-bound, against the dense MFMA peak of the workload's type),
+from HIP events recorded on the launch stream around every phase-1 launch in
+the timed steps; ``roofline_query`` is for the query step against the larger
+of its two bounds; ``roofline_phase2`` is for the decode step (HBM-bound),
+from events around the whole decode loop (every step's launches: append and
+partials in one, then the merge; fp32: append, partials, merge) divided by
+the steps. ``cpu_baseline`` is the fp64 oracle timed on a bounded sample on
+the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 (NAME: a workload of the scope table, default the 128K one, or a sweep
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "phase-1 ctx tokens/s + phase-2 decode µs/token at 128K, % of roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -84,17 +87,22 @@ def query_work(w):
     return flop, append + kv + q + parts + out
 
 
+def mfma_peak(w) -> float:
+    """The dense MFMA peak of the workload's arithmetic type, TFLOP/s."""
+    return PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+
+
 def query_roofline(w, q_ms: float) -> dict:
     """The query step against the larger of its two bounds (MFMA time of its
-    FLOP at the bf16 peak, HBM time of its bytes at 8 TB/s)."""
+    FLOP at the MFMA peak of its type, HBM time of its bytes at 8 TB/s)."""
     flop, nbytes = query_work(w)
-    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_mfma = flop / (mfma_peak(w) * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     t = q_ms * 1e-3
     if t_hbm >= t_mfma:
         r = {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        r = {"bound": "mfma", "achieved": flop / t / 1e12, "peak": PEAK_BF16_TFLOPS,
+        r = {"bound": "mfma", "achieved": flop / t / 1e12, "peak": mfma_peak(w),
              "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
     r["frac_other_bound"] = min(t_mfma, t_hbm) / t
@@ -507,12 +515,21 @@ def main():
 
     pg = "true" if args.paged else "false"
     rp = {"none": 0, "original": 1, "adjacent": 2}[args.rope]
-    kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}, false>"
-    # the decode kernel's instantiation that splits a 32-key slice at a host
-    # boundary serves contexts and blocks off the slice grid
-    mid = "true" if (w.ctx_len % 32 or w.block_len % 32) else "false"
-    kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}, {mid}>",
-              f"lse_merge_kernel<{w.head_dim}>")
+    if w.dtype == "f32":
+        # fp32 runs on the matrix-core fp32 kernel; its decode step is three
+        # launches: the append, the partials, the merge
+        kname1 = f"attn_f32m_kernel<{w.head_dim}, true, false, {rp}>"
+        kname2 = (f"kv_write_kernel<float, {w.head_dim}, {pg}, false>",
+                  f"attn_f32m_kernel<{w.head_dim}, false, {pg}, 0>",
+                  f"lse_merge_kernel<{w.head_dim}>")
+    else:
+        kname1 = f"attn_wide_kernel<{w.head_dim}, 8, 1, true, false, {rp}, false>"
+        # the decode kernel's instantiation that splits a 32-key slice at a
+        # host boundary serves contexts and blocks off the slice grid
+        mid = "true" if (w.ctx_len % 32 or w.block_len % 32) else "false"
+        kname2 = (f"attn_decode_kernel<{w.head_dim}, true, {pg}, {mid}>",
+                  f"lse_merge_kernel<{w.head_dim}>")
+    pk = mfma_peak(w)
     bcfg = {"workload": args.workload, "paged": bool(args.paged), "rope": args.rope}
     t1, t2 = load_traffic(bcfg, kname1), load_traffic(bcfg, *kname2)
     # the shader clock phase 1 runs at (outside the timed region)
@@ -550,8 +567,8 @@ def main():
         "query_step_ms": q_ms,
         "decode_us_per_step": step_us,
         "decode_us_per_token": step_us / w.batch,
-        "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": p1_tflops / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": p1_tflops, "peak": pk,
+                     "unit": "TFLOP/s", "frac": p1_tflops / pk,
                      "traffic": t1, "kernel": kname1,
                      "algorithmic": f"{flops:.4e} FLOP per launch (4*d per visible pair)"},
         "roofline_phase2": {"bound": "hbm", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,

@@ -141,3 +141,15 @@ def test_counter_summary_is_per_dispatch(tmp_path):
     assert "SQ_INSTS_MFMA                    1.000000e+03" in text
     assert "effective engine clock (active / duration) 2.000 GHz" in text
     assert "non-MFMA VALU instructions per MFMA        4.80" in text
+
+
+def test_mfma_peak_follows_the_workload_type():
+    """fp32 workloads run on the fp32 matrix cores: their MFMA roofline is
+    the dense fp32 peak (157.3 TFLOP/s), not the bf16 one."""
+    import bench
+    f32, bf16 = syn.workload("tiny_f32"), syn.workload("llama8b_32k")
+    assert bench.mfma_peak(f32) == 157.3 and bench.mfma_peak(bf16) == 2500.0
+    # a query step made MFMA-bound at fp32 is priced against the fp32 peak
+    r = bench.query_roofline(f32.__class__(**{**f32.__dict__, "n_query": 256, "ctx_len": 4096,
+                                              "block_len": 1024, "anchor_len": 1024}), 1.0)
+    assert r["bound"] == "mfma" and r["peak"] == 157.3, r
