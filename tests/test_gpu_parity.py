@@ -74,6 +74,10 @@ CASES = {
     # (as the 1M workload's 32 query rows): the waves holding rows 32..63 only
     # load tiles and meet barriers, and their SIMD partners do the arithmetic
     "short_tile_g4": W("short_tile_g4", 1, 8, 2, 128, 2100, 512, 300, 24, 2, "bf16", seed=24),
+    # fp32 on two sequences: ragged last block, anchor shorter than the block
+    # and off the 32-key grid, so a workgroup's slices mix anchor and block
+    # keys and its four waves take different numbers of them
+    "f32_b2_ragged": W("f32_b2_ragged", 2, 4, 2, 64, 333, 100, 37, 5, 2, "f32", seed=25),
 }
 EMPTY_SPLIT_CASES = ("long_tail_wide", "ragged_empty_split")
 
@@ -139,7 +143,8 @@ def test_phase2_query_and_decode_match_oracle(runs, name):
 @pytest.mark.parametrize("name", ["gqa4_d128_ragged", "g1_unaligned_a_lt_b", "g2_d64_wide_tail",
                                   "g8_narrow", "f32_gqa_d128", "long_tail_wide",
                                   "ragged_empty_split", "balanced_bnd", "balanced_b2_g8_d64",
-                                  "b1_a1", "ctx1", "b1_wide_tail", "f32_b1", "short_tile_g4"])
+                                  "b1_a1", "ctx1", "b1_wide_tail", "f32_b1", "short_tile_g4",
+                                  "f32_b2_ragged"])
 def test_partials_are_the_hosts_replies(runs, name):
     """Each split's (vector, scalar) equals the oracle's host reply on that range."""
     p, _, _, _ = _pipeline(runs, name)
@@ -317,7 +322,7 @@ def test_binding_rejects_wrong_buffers():
                                   "g1_unaligned_a_lt_b", "tiny_f32", "g4_d64_many_blocks",
                                   "balanced_bnd", "balanced_b2_g8_d64", "b1_a1", "ctx1",
                                   "f32_b1", "b1_wide_tail", "g2_d64_wide_tail", "long_tail_wide",
-                                  "kv_major_g8", "many_rows_d64", "short_tile_g4"])
+                                  "kv_major_g8", "many_rows_d64", "short_tile_g4", "f32_b2_ragged"])
 def test_fused_decode_step(runs, name):
     """star_attn_decode_step (append + partials + merge) against the oracle's
     decode loop and against the three separate calls, every step: the query
