@@ -217,8 +217,8 @@ STAR_HD static inline void wide_map(int64_t bid, bool phase1, int32_t NG, int32_
   }
 }
 
-// fp32 MFMA kernel: one wave (and workgroup) per 32 columns.
-// Phase 1: wave -> (sequence s, head h, row group rg); its columns are the
+// fp32 MFMA kernel: one workgroup per 32 columns.
+// Phase 1: workgroup -> (sequence s, head h, row group rg); its columns are the
 // context rows 32 rg .. 32 rg + 31 of head h.
 STAR_HD static inline void f32m_phase1_map(int64_t wid, int64_t L, int32_t Hq, int64_t* s,
                                            int32_t* h, int64_t* rg) {
@@ -228,7 +228,7 @@ STAR_HD static inline void f32m_phase1_map(int64_t wid, int64_t L, int32_t Hq, i
   *h = (int32_t)(t % Hq);
   *s = t / Hq;
 }
-// Phase 2: wave -> (sequence s, kv head kvh, column group cg, split sigma);
+// Phase 2: workgroup -> (sequence s, kv head kvh, column group cg, split sigma);
 // column c of group cg is query row (32 cg + c) / G of head kvh * G + (32 cg + c) % G.
 STAR_HD static inline void f32m_phase2_map(int64_t wid, int32_t n_split, int64_t ncg, int32_t Hkv,
                                            int64_t* s, int32_t* kvh, int64_t* cg,
@@ -240,7 +240,7 @@ STAR_HD static inline void f32m_phase2_map(int64_t wid, int32_t n_split, int64_t
   *kvh = (int32_t)(t % Hkv);
   *s = t / Hkv;
 }
-// Column c (0..31) of an fp32 MFMA wave: its row of q, head, whether it is a
+// Column c (0..31) of an fp32 MFMA workgroup: its row of q, head, whether it is a
 // live column, and the keys it sees: [0, hiA) and [loB, hiB) (phase 1: the
 // anchor for blocks >= 1, then its block causally; phase 2: split rows
 // [lo, hi) up to its own position). Phase 1: rg is the row group and h the
@@ -274,7 +274,7 @@ STAR_HD static inline F32mCol f32m_column(bool phase1, int c, int64_t rg_or_cg, 
   }
   return x;
 }
-// The keys an fp32 MFMA wave loads: [0, kA) and [kB0, kB1), the union of its
+// The keys an fp32 MFMA workgroup loads: [0, kA) and [kB0, kB1), the union of its
 // live columns' ranges; a 32-key slice [k0, k0 + 32) is processed when it
 // meets them (f32m_slice).
 STAR_HD static inline void f32m_wave_keys(bool phase1, int64_t rg_or_cg, int32_t h, int64_t L,
@@ -471,7 +471,7 @@ static inline int64_t kv_write_grid(const Dims& d, int64_t pos0, int64_t n_tok) 
   return ((pos0 + n_tok - 1) / kTile - pos0 / kTile + 1) * d.B * d.Hkv;
 }
 
-// phase 1: bf16 wide kernel (512 threads), or one wave per 32 rows of a head (fp32)
+// phase 1: bf16 wide kernel (512 threads), or one workgroup per 32 rows of a head (fp32)
 static inline bool phase1_fits(const Dims& d) {
   if (d.dtype == STAR_F32) return grid_fits(f32m_phase1_grid(d), 64 * f32m_waves(d.D));
   return grid_fits(phase1_geom(d).grid, 64 * kWideWaves);

@@ -1689,9 +1689,11 @@ struct F32Args {
 
 // ---------------------------------------------------------------------------
 // fp32 on the matrix cores (phase 1, with or without a rotary embedding, and
-// the phase-2 partials): one wave per 32 columns, v_mfma_f32_32x32x2_f32 for both
-// products. Per 32-key slice the K rows and the V rows (turned back from the
-// transposed tile) are staged in LDS, rows outside the wave's key range zero;
+// the phase-2 partials): one workgroup per 32 columns, v_mfma_f32_32x32x2_f32
+// for both products; the workgroup's 32-key slices are dealt round robin to
+// its waves, whose states merge at the end. Per slice the K rows and the V
+// rows (turned back from the transposed tile) are staged in the wave's LDS
+// buffers, rows outside the workgroup's key range zero;
 // S^T = K Q^T (A: K[key][2 ks + g], B: Q[column][2 ks + g]); each lane then
 // holds column l32 and keys 8 (r / 4) + 4 g + r % 4 of the slice; the online
 // softmax runs per column in fp32 (the lane pair l32, l32 + 32 shares a
@@ -1731,7 +1733,7 @@ __global__ __launch_bounds__(64 * f32m_waves(D)) void attn_f32m_kernel(const F32
   float* const sP = sPw + w * 32 * 33;
   const int64_t wid = blockIdx.x;
 
-  // the wave's columns: column c -> (token row in q, head), valid, and its
+  // the workgroup's columns: column c -> (token row in q, head), valid, and its
   // visible keys: [0, hiA) (phase 1) and [loB, hiB) up to its position
   int64_t s, ncg = 0, rg = 0, cg = 0;
   int32_t h0 = 0, kvh, sigma = 0;
@@ -1750,7 +1752,7 @@ __global__ __launch_bounds__(64 * f32m_waves(D)) void attn_f32m_kernel(const F32
     return f32m_column(PHASE1, c, PHASE1 ? rg : cg, PHASE1 ? h0 : kvh, a.L, a.blk, a.anc,
                        a.q_tokens, a.G, a.kv_len, lo, hi);
   };
-  // the wave's key range: the union of its columns' ranges (wave-uniform)
+  // the workgroup's key range: the union of its columns' ranges (uniform)
   int64_t kA, kB0, kB1;
   f32m_wave_keys(PHASE1, PHASE1 ? rg : cg, PHASE1 ? h0 : kvh, a.L, a.blk, a.anc, a.q_tokens, a.G,
                  a.kv_len, lo, hi, &kA, &kB0, &kB1);
@@ -1762,7 +1764,7 @@ __global__ __launch_bounds__(64 * f32m_waves(D)) void attn_f32m_kernel(const F32
     else return t * 64 * D;
   };
   // the keys of slice [k0, k0 + 32) that are loaded (else zero): those some
-  // column of the wave may see, as a bit mask
+  // column of the workgroup may see, as a bit mask
   auto slice_bits = [&](int64_t k0) { return range_bits(0, kA, k0) | range_bits(kB0, kB1, k0); };
   // x, or +0 where bit j of m is clear, on the bits: the pieces hold the
   // unwritten (possibly NaN) rows next to wanted keys, and a floating-point
@@ -2254,7 +2256,7 @@ static int phase1_impl(const Dims& d, const void* kc, const void* vc, const void
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     a.q_tokens = d.L;
-    // the matrix cores: one wave per 32 context rows of a head
+    // the matrix cores: one workgroup per 32 context rows of a head
     if (!grid_fits(f32m_phase1_grid(d), 64 * f32m_waves(d.D))) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)f32m_phase1_grid(d));
     const dim3 block((unsigned)(64 * f32m_waves(d.D)));
@@ -2368,9 +2370,9 @@ static int phase2_partial_impl(const Dims& d, const Plan& p, const void* kc, con
     a.tail_len = p.tail_len;
     a.per_block = p.per_block;
     a.n_split = p.n_split;
-    // the matrix cores: one wave per 32 (query row, head) columns of a kv head and split
+    // the matrix cores: one workgroup per 32 (query row, head) columns of a kv head and split
     const int64_t n = f32m_phase2_grid(d, p, n_query);
-    if (!grid_fits(n, 64)) return STAR_ERR_SHAPE;
+    if (!grid_fits(n, 64 * f32m_waves(d.D))) return STAR_ERR_SHAPE;
     const dim3 grid((unsigned)n);
     const dim3 block((unsigned)(64 * f32m_waves(d.D)));
     if (d.D == 128) hipLaunchKernelGGL((attn_f32m_kernel<128, false, PAGED, kRopeNone>), grid, block, 0, st, a);
