@@ -1,7 +1,8 @@
 """The decode step inside a HIP graph: eight star_attn_decode_step calls
-(each one append + split partials + merge, two launches) captured once and
-replayed three times, with eager work and synchronisation between replays,
-give bit-identical outputs to the eager calls every time. The library
+(each one append + split partials + merge: two launches in bf16, three in
+fp32) captured once and replayed three times, with eager work and
+synchronisation between replays, give bit-identical outputs to the eager
+calls every time. The library
 allocates nothing, synchronises nothing and issues no memset, so a serving
 loop can capture its decode steps."""
 import numpy as np
@@ -16,10 +17,18 @@ pytestmark = pytest.mark.gpu
 STEPS = 8
 
 
-def test_decode_steps_replay_in_a_graph():
+GRAPH_WORKLOADS = {
+    "bf16": syn.Workload("graph", 1, 8, 2, 128, 1536, 512, 256, 4, STEPS, "bf16", seed=41),
+    # fp32: the append, the matrix-core partials (four-wave workgroups at d = 64), the merge
+    "f32": syn.Workload("graph_f32", 1, 4, 2, 64, 600, 256, 128, 4, STEPS, "f32", seed=42),
+}
+
+
+@pytest.mark.parametrize("dtype", list(GRAPH_WORKLOADS))
+def test_decode_steps_replay_in_a_graph(dtype):
     if not torch.cuda.is_available():
         pytest.skip("no GPU in this environment")
-    w = syn.Workload("graph", 1, 8, 2, 128, 1536, 512, 256, 4, STEPS, "bf16", seed=41)
+    w = GRAPH_WORKLOADS[dtype]
     p = Pipeline(w, threads=1)
     p.write_context()
     p.query_step()

@@ -1,4 +1,4 @@
-"""Two workloads run at once from two host threads, each on its own stream
+"""Three workloads run at once from three host threads, each on its own stream
 (default priority), give bit-identical results to the same workloads run one
 after the other on the default stream: every entry point runs on the stream
 it is given, and the library keeps no state between calls."""
@@ -20,6 +20,8 @@ WORKLOADS = [
     W("streams_a", 1, 8, 2, 128, 2172, 1024, 300, 8, 4, "bf16", seed=31),
     # blockwise plan, d = 64, two sequences, GQA 8:1, a wide query step
     W("streams_b", 2, 16, 2, 64, 700, 64, 64, 40, 4, "bf16", seed=32),
+    # fp32 on the matrix cores: two-wave workgroups at d = 128
+    W("streams_f32", 1, 4, 2, 128, 500, 128, 100, 6, 3, "f32", seed=33),
 ]
 
 
