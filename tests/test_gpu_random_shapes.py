@@ -1,7 +1,8 @@
 """A seeded sweep of small random shapes through the whole path, against the
 fp64 oracle: phase 1, then the query step and every decode step, each as one
 star_attn_decode_step call and again as separate calls (append, partials,
-merge). The shapes mix batch, GQA ratio (1 to 8), head dimension, contexts
+merge), and on a paged cache, whose results must be the contiguous cache's
+bits. The shapes mix batch, GQA ratio (1 to 8), head dimension, contexts
 from one token up, blocks from one row to longer than the context, anchors
 shorter than the block and off the 32-key grid, and query steps from one
 token to a wide tile, in bf16 and fp32. They come from a fixed seed, so the
@@ -11,7 +12,7 @@ import pytest
 import torch
 
 from long_context_attention_phase1_amd import synthetic as syn
-from long_context_attention_phase1_amd.pipeline import Pipeline, to_host_f64
+from long_context_attention_phase1_amd.pipeline import PagedPipeline, Pipeline, to_host_f64
 from oracle import star_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -62,7 +63,12 @@ def test_random_shape_matches_oracle(w):
     q = Pipeline(w, inputs=p.inputs, threads=4)
     q.write_context()
     sep_o, sep_l = q.run_tail(fused=False)
+    # the paged cache (a random page permutation) gives the contiguous cache's bits
+    r = PagedPipeline(w, inputs=p.inputs, threads=4)
+    r.write_context()
+    pg_o, pg_l = r.run_tail(fused=True)
     torch.cuda.synchronize()
+    assert np.array_equal(pg_o, fused_o) and np.array_equal(pg_l, fused_l), w.name
 
     x = {k: syn.to_f64(v, w.dtype) for k, v in p.inputs.items()}
     sc = orc.resolve_scale(w.head_dim, 0.0)
