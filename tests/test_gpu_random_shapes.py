@@ -2,7 +2,7 @@
 fp64 oracle: phase 1, then the query step and every decode step, each as one
 star_attn_decode_step call and again as separate calls (append, partials,
 merge), and on a paged cache, whose results must be the contiguous cache's
-bits. The shapes mix batch, GQA ratio (1 to 8), head dimension, contexts
+bits; and phase 1 with the rotary embedding in both anchor position-id modes. The shapes mix batch, GQA ratio (1 to 8), head dimension, contexts
 from one token up, blocks from one row to longer than the context, anchors
 shorter than the block and off the 32-key grid, and query steps from one
 token to a wide tile, in bf16 and fp32. They come from a fixed seed, so the
@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_attention_phase1_amd as sa
 from long_context_attention_phase1_amd import synthetic as syn
 from long_context_attention_phase1_amd.pipeline import PagedPipeline, Pipeline, to_host_f64
 from oracle import star_oracle as orc
@@ -83,3 +84,17 @@ def test_random_shape_matches_oracle(w):
     assert np.isfinite(o1).all() and e1 <= TOL[w.dtype]
     for eo, el in errs:
         assert eo <= TOL[w.dtype] and el <= TOL_LSE[w.dtype]
+
+    # phase 1 with the rotary embedding fused in, both anchor position-id modes
+    for mode, omode, mname in ((sa.STAR_ROPE_ORIGINAL, orc.ROPE_ORIGINAL, "original"),
+                               (sa.STAR_ROPE_ADJACENT, orc.ROPE_ADJACENT, "adjacent")):
+        rope = p.rope(mode)
+        p.write_context_rope(rope)
+        o = to_host_f64(p.phase1_rope(rope))
+        torch.cuda.synchronize()
+        c, sn = (t.astype(np.float64) for t in p.rope_host)
+        ref = orc.phase1_rope(x["q_ctx"], x["k_ctx"], x["v_ctx"], w.block_len, w.anchor_len, sc,
+                              c, sn, omode)
+        er = float(np.max(np.abs(o - ref)))
+        print(f"{w.name}: phase 1 with rotary ids ({mname}) {er:.2e}")
+        assert er <= TOL[w.dtype], (w.name, mname)
